@@ -1,0 +1,162 @@
+"""Kimi Delta Attention hot path on MI355X: thin Python binding of libkda.so.
+
+The functions below carry the C ABI's names (``include/kda.h``) and only
+marshal arguments: they check devices, dtypes, shapes and contiguity, allocate
+outputs with torch when the caller gives none, and pass raw device pointers
+and the current HIP stream. Every step of the computation runs in the HIP
+kernels behind the library; there is no other code path. If the library is
+missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "KDAError", "lib_path", "load_library", "kda_status_string",
+    "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_decode_step",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+KDA_F32, KDA_BF16 = 0, 1
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {kda_status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build the HIP library first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_prefill_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                    vp, sz, vp]
+    lib.kda_prefill_fwd.restype = i
+    lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, vp]
+    lib.kda_decode_step.restype = i
+    _lib = lib
+    return lib
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kda_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int,
+                               dtype: torch.dtype, chunk: int = 64) -> int:
+    return int(load_library().kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[dtype], chunk))
+
+
+def kda_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    log_alpha: torch.Tensor, beta: torch.Tensor,
+                    S0: Optional[torch.Tensor] = None, *, chunk: int = 64,
+                    o: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                    want_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill. q,k,log_alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
+    S0 [B,H,dk,dv] fp32 or None. Returns (o [B,T,H,dv], S_final fp32 or None)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_prefill_fwd needs GPU tensors")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, T, H, dk), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, T, H, dv), dt, dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = kda_prefill_workspace_size(B, T, H, dk, dv, dt, chunk)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                             _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
+                             _ptr(workspace), wsz, _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_fwd")
+    return o, S_final
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    log_alpha: torch.Tensor, beta: torch.Tensor, S: torch.Tensor, *,
+                    o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step; S [B,H,dk,dv] fp32 is updated in place. Returns o [B,H,dv]."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_decode_step needs GPU tensors")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (B, H, dk), dt, dev)
+    _check(k, "k", (B, H, dk), dt, dev)
+    _check(v, "v", (B, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, H, dk), torch.float32, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, H, dv), dt, dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                             _ptr(o), B, H, dk, dv, _DTYPES[dt], _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,137 @@
+// C ABI of the KDA hot path: argument validation on the host, then dispatch
+// to the HIP kernels on the caller's stream. Nothing here allocates,
+// synchronises or keeps state between calls.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 0 || c == 16 || c == 32 || c == 64; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi)
+    Range() = default;
+    Range(const void* p, size_t bytes) : lo((uintptr_t)p), hi((uintptr_t)p + bytes) {}
+    bool empty() const { return lo == hi; }
+};
+bool overlap(const Range& a, const Range& b) {
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// a * b * ... without size_t overflow; false on overflow
+bool mul_ok(size_t& acc, size_t x) {
+    if (x != 0 && acc > SIZE_MAX / x) return false;
+    acc *= x;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                                  int chunk) {
+    (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)dtype; (void)chunk;
+    return 0;  // the fused kernels keep every intermediate on chip
+}
+
+kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* S0, void* o, float* S_final,
+                           int B, int T, int H, int dk, int dv,
+                           kda_dtype dtype, int chunk,
+                           void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (ws_bytes < kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk))
+        return KDA_ERR_WORKSPACE;
+    (void)ws;
+    if (B == 0 || H == 0) return KDA_OK;
+
+    const size_t elt = dtype == KDA_BF16 ? 2 : 4;
+    size_t tok = 1;
+    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H))
+        return KDA_ERR_INVALID_ARG;
+    size_t nk = tok, nv = tok, ns = (size_t)B * (size_t)H;
+    if (!mul_ok(nk, (size_t)dk) || !mul_ok(nv, (size_t)dv) || !mul_ok(ns, (size_t)dk * dv))
+        return KDA_ERR_INVALID_ARG;
+    if (nk > (SIZE_MAX >> 3) || nv > (SIZE_MAX >> 3) || ns > (SIZE_MAX >> 3))
+        return KDA_ERR_INVALID_ARG;
+
+    if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_final};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+
+    const Range rq(q, T ? nk * elt : 0), rk(k, T ? nk * elt : 0), rv(v, T ? nv * elt : 0);
+    const Range rla(log_alpha, T ? nk * 4 : 0), rb(beta, T ? tok * 4 : 0);
+    const Range rs0(S0, S0 ? ns * 4 : 0), ro(o, T ? nv * elt : 0);
+    const Range rsf(S_final, S_final ? ns * 4 : 0);
+    const Range inputs[] = {rq, rk, rv, rla, rb, rs0};
+    for (const Range& in : inputs)
+        if (overlap(ro, in) || overlap(rsf, in)) {
+            // the only permitted overlap: S_final is exactly S0
+            if (&in == &inputs[5] && rsf.lo == rs0.lo && !overlap(ro, in)) continue;
+            return KDA_ERR_INVALID_ARG;
+        }
+    if (overlap(ro, rsf)) return KDA_ERR_INVALID_ARG;
+
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
+        e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, st);
+    else
+        e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
+                                        S_final, B, T, H, dk, dv, chunk ? chunk : 64, st);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           float* S, void* o,
+                           int B, int H, int dk, int dv,
+                           kda_dtype dtype, void* stream) {
+    if (B < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_INVALID_ARG;
+    const size_t elt = dtype == KDA_BF16 ? 2 : 4;
+    size_t bh = 1;
+    if (!mul_ok(bh, (size_t)B) || !mul_ok(bh, (size_t)H)) return KDA_ERR_INVALID_ARG;
+    if (bh > (size_t)INT32_MAX / 4) return KDA_ERR_INVALID_ARG;
+    const size_t nk = bh * dk, nv = bh * dv, ns = bh * dk * dv;
+    const Range rq(q, nk * elt), rk(k, nk * elt), rv(v, nv * elt), rla(log_alpha, nk * 4),
+        rb(beta, bh * 4), rS(S, ns * 4), ro(o, nv * elt);
+    const Range ins[] = {rq, rk, rv, rla, rb};
+    for (const Range& in : ins)
+        if (overlap(ro, in) || overlap(rS, in)) return KDA_ERR_INVALID_ARG;
+    if (overlap(ro, rS)) return KDA_ERR_INVALID_ARG;
+
+    const hipError_t e = kda::launch_decode(dtype == KDA_BF16, dk, dv, q, k, v, log_alpha,
+                                            beta, S, o, (int)bh, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Shared device helpers for the KDA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    bf16 b = (bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ float bf16_from_bits(uint16_t u) {
+    return __builtin_bit_cast(float, (uint32_t)u << 16);
+}
+
+// Pack four fp32 into the 4 x bf16 operand of v_mfma_f32_16x16x16_bf16.
+__device__ __forceinline__ s16x4 pack4(f32x4 v) {
+    s16x4 r;
+    r[0] = (short)bf16_bits(v[0]);
+    r[1] = (short)bf16_bits(v[1]);
+    r[2] = (short)bf16_bits(v[2]);
+    r[3] = (short)bf16_bits(v[3]);
+    return r;
+}
+
+// Pack 2 x 4 fp32 into the 8 x bf16 operand of v_mfma_f32_16x16x32_bf16.
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+    r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+    r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+    return r;
+}
+
+// D(16x16,f32) += A(16x32) * B(32x16), bf16 operands.
+// Lane l holds A[l%16][8(l/16)..+7], B[8(l/16)..+7][l%16], D[4(l/16)..+3][l%16].
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// D(16x16,f32) += A(16x16) * B(16x16), bf16 operands.
+// Lane l holds A[l%16][4(l/16)..+3], B[4(l/16)..+3][l%16], D[4(l/16)..+3][l%16].
+__device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Natural exponential through the hardware exp2 (v_exp_f32).
+__device__ __forceinline__ float exp_e(float x) { return __expf(x); }
+
+// Wait until this wave's LDS operations have completed.
+__device__ __forceinline__ void lds_fence_wave() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace kda

@@ -1,0 +1,144 @@
+// One-token KDA decode step, streaming each fp32 state once from HBM.
+//
+// Per head ("Kimi K3: the manos...", section "FlashKDA Algorithm", the
+// per-token form; Kimi K3 blog, "Decay Old Memory" / "Apply Delta-Rule
+// Update"):
+//     Sbar = Diag(alpha) S            alpha = exp(log_alpha), per key channel (row)
+//     w    = Sbar^T k,  p = Sbar^T q  (reductions over the dk rows)
+//     u    = beta (v - w)
+//     S    = Sbar + k u^T             (written back in place)
+//     o    = S^T q = p + u (k . q)    (same pass: no second read of S)
+// The section's complexity analysis counts ~7 dk*dv flops and 8 dk*dv bytes
+// (fp32 read + write) per head: the kernel is HBM-bound, so the design goal is
+// exactly one coalesced read and one write of every state element.
+//
+// Mapping: one wave owns one head and a slice of NC (<= 32) columns. Lane
+// (cg, rg) holds a float4 of columns and RPL consecutive rows, so each load
+// instruction of the wave covers NRG rows x NC*4 bytes. The column reductions
+// over rows are xor-shuffles across the NRG lanes sharing a column group.
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <typename T, int N>
+__device__ __forceinline__ void load_row_vals(const T* __restrict__ p, float (&out)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = to_f32(p[i]);
+}
+
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    float* __restrict__ S, T* __restrict__ o, int BH)
+{
+    constexpr int NC = DV < 32 ? DV : 32;   // columns per wave
+    constexpr int NCG = NC / 4;             // float4 column groups
+    constexpr int NRG = kWave / NCG;        // row groups
+    constexpr int RPL = DK / NRG;           // rows per lane
+    constexpr int SLICES = DV / NC;
+    static_assert(RPL >= 1 && RPL * NRG == DK, "dk must cover every row group");
+
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int head = gw / SLICES;
+    if (head >= BH) return;
+    const int slice = gw - head * SLICES;
+    const int cg = lane % NCG;
+    const int rg = lane / NCG;
+    const int col = slice * NC + cg * 4;
+    const int row0 = rg * RPL;
+
+    float* Sh = S + (size_t)head * DK * DV;
+    f32x4 s[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+        s[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+
+    float kr[RPL], qr[RPL], lar[RPL];
+    load_row_vals<T, RPL>(k + (size_t)head * DK + row0, kr);
+    load_row_vals<T, RPL>(q + (size_t)head * DK + row0, qr);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) lar[r] = log_alpha[(size_t)head * DK + row0 + r];
+    float vv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[(size_t)head * DV + col + c]);
+    const float b = beta[head];
+
+    // Decay rows, then the two column reductions and k.q over this lane's rows.
+    f32x4 w = zero4(), p = zero4();
+    float kq = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const float a = exp_e(lar[r]);
+        s[r] *= a;
+        w += s[r] * kr[r];
+        p += s[r] * qr[r];
+        kq += kr[r] * qr[r];
+    }
+#pragma unroll
+    for (int off = NCG; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            w[c] += __shfl_xor(w[c], off);
+            p[c] += __shfl_xor(p[c], off);
+        }
+        kq += __shfl_xor(kq, off);
+    }
+
+    f32x4 u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[c] = b * (vv[c] - w[c]);
+
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const f32x4 sn = s[r] + kr[r] * u;
+        __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+    }
+
+    if (rg == 0) {
+        T* oh = o + (size_t)head * DV + col;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) oh[c] = from_f32<T>(p[c] + u[c] * kq);
+    }
+}
+
+template <int DK, int DV, typename T>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* la,
+                                  const float* beta, float* S, void* o, int BH, hipStream_t st)
+{
+    constexpr int NC = DV < 32 ? DV : 32;
+    const long waves = (long)BH * (DV / NC);
+    const int threads = 256;
+    const long blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), dim3((unsigned)blocks), dim3(threads), 0, st,
+                       (const T*)q, (const T*)k, (const T*)v, la, beta, S, (T*)o, BH);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_dv(int dk, int dv, const void* q, const void* k, const void* v,
+                              const float* la, const float* beta, float* S, void* o, int BH,
+                              hipStream_t st)
+{
+#define KDA_DEC_CASE(DKV, DVV) \
+    if (dk == DKV && dv == DVV) return launch_decode_t<DKV, DVV, T>(q, k, v, la, beta, S, o, BH, st);
+    KDA_DEC_CASE(16, 16) KDA_DEC_CASE(16, 32) KDA_DEC_CASE(16, 64) KDA_DEC_CASE(16, 128)
+    KDA_DEC_CASE(32, 16) KDA_DEC_CASE(32, 32) KDA_DEC_CASE(32, 64) KDA_DEC_CASE(32, 128)
+    KDA_DEC_CASE(64, 16) KDA_DEC_CASE(64, 32) KDA_DEC_CASE(64, 64) KDA_DEC_CASE(64, 128)
+    KDA_DEC_CASE(128, 16) KDA_DEC_CASE(128, 32) KDA_DEC_CASE(128, 64) KDA_DEC_CASE(128, 128)
+#undef KDA_DEC_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(bool bf16_io, int dk, int dv, const void* q, const void* k,
+                         const void* v, const float* la, const float* beta, float* S,
+                         void* o, int BH, hipStream_t st)
+{
+    if (bf16_io) return dispatch_dv<bf16>(dk, dv, q, k, v, la, beta, S, o, BH, st);
+    return dispatch_dv<float>(dk, dv, q, k, v, la, beta, S, o, BH, st);
+}
+
+}  // namespace kda

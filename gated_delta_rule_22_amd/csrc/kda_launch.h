@@ -1,0 +1,27 @@
+// Internal launchers behind the C ABI (shapes already validated by the caller).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+// Decode step over B*H heads.
+hipError_t launch_decode(bool bf16_io, int dk, int dv, const void* q, const void* k,
+                         const void* v, const float* la, const float* beta, float* S,
+                         void* o, int BH, hipStream_t st);
+
+// Generic chunked prefill (fp32 arithmetic, any supported dk/dv/chunk, fp32 or bf16 I/O).
+hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, const void* v,
+                                  const float* la, const float* beta, const float* S0,
+                                  void* o, float* S_final, int B, int T, int H, int dk,
+                                  int dv, int chunk, hipStream_t st);
+
+// bf16 MFMA chunked prefill for dk = dv = 128, chunk 64. Returns
+// hipErrorInvalidValue if the shape is not one it implements.
+bool prefill_mfma_supported(int dk, int dv, int chunk);
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
+                               const float* beta, const float* S0, void* o, float* S_final,
+                               int B, int T, int H, hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,111 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention hot path.
+ *
+ * The operation (Kimi K3 blog, section "Kimi Delta Attention"; the
+ * trillion-scale architecture page, section 4 "The KDA update, in plain
+ * words"), per batch b and head h, for tokens t = 0..T-1:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,            alpha_t = exp(log_alpha_t) (per key channel)
+ *
+ * with state S in R^{dk x dv} per head. No scale factor is applied to q, and
+ * q, k are not normalised here (the Kimi Linear layer L2-normalises them
+ * before the op: "Kimi K3: the manos...", section "Kimi Linear").
+ *
+ * Layouts (row-major, contiguous, device memory):
+ *     q, k, log_alpha   [B, T, H, dk]   q, k in `dtype`; log_alpha fp32 (natural log)
+ *     v, o              [B, T, H, dv]   in `dtype`
+ *     beta              [B, T, H]       fp32, used as given (no clamp)
+ *     S0, S_final, S    [B, H, dk, dv]  fp32, dv contiguous
+ * Decode drops the T axis.
+ *
+ * Ownership: the caller owns every buffer. The library allocates no device
+ * memory in these calls, never frees and never synchronises; work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
+ * asynchronously, so a device fault surfaces at the caller's next
+ * synchronisation. The library keeps no state between calls and is
+ * reentrant.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * launched; a rejected call has no side effect. KDA_ERR_HIP reports a launch
+ * failure (hipGetLastError after the launch).
+ *
+ * Supported on the GPU: dk, dv in {16, 32, 64, 128}; chunk in {0 (=64), 16,
+ * 32, 64}; dtype fp32 or bf16. All device pointers must be 16-byte aligned.
+ * The log-decay is meant to lie in [-5, 0] per step (the bound stated on the
+ * trillion-scale page, section 4); results stay finite for that range.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment, aliasing */
+    KDA_ERR_UNSUPPORTED = 2,   /* dk, dv, chunk or dtype outside the supported set */
+    KDA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    KDA_ERR_HIP = 4            /* a HIP call or kernel launch failed */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,               /* q, k, v, o are fp32 */
+    KDA_BF16 = 1               /* q, k, v, o are bf16 (fp32 state and accumulation) */
+} kda_dtype;
+
+/*
+ * Bytes of device workspace kda_prefill_fwd needs for these sizes (0 if
+ * none). Returns 0 also for arguments it would reject.
+ */
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv,
+                                  kda_dtype dtype, int chunk);
+
+/*
+ * Chunk-parallel prefill ("Kimi K3: the manos...", section "FlashKDA
+ * Algorithm": chunk-local cumulative decay, K/Q decay scaling, the UT
+ * transform U = (I + L)^{-1} Diag(beta)(V - K_decay S_in), the causal
+ * M_qk = tril(Q_decay K_inv^T) output term and the S_in -> S_out carry).
+ *
+ *   q, k, v, log_alpha, beta   inputs (required when T > 0)
+ *   S0       initial state, or NULL for zeros
+ *   o        output [B,T,H,dv] in `dtype` (required when T > 0); must not
+ *            overlap any input
+ *   S_final  final state, or NULL to skip; may be the same buffer as S0
+ *            (in-place continuation), must not partially overlap it
+ *   chunk    tokens per chunk, 0 = 64. It selects the blocking only; the
+ *            result is the same recurrence for any value.
+ *   ws, ws_bytes  device workspace of at least kda_prefill_workspace_size()
+ *            bytes (may be NULL/0 when that size is 0)
+ * T = 0 writes S_final = S0 (or zeros) and no o.
+ */
+kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* S0, void* o, float* S_final,
+                           int B, int T, int H, int dk, int dv,
+                           kda_dtype dtype, int chunk,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One-token decode step (the recurrence above for a single t, the form
+ * "Kimi K3: the manos..." section "FlashKDA Algorithm" gives as
+ * u = beta (v - (D S)^T k), S = D S + k u^T, o^T = q^T S), updating S in
+ * place. q, k, log_alpha [B,H,dk]; v, o [B,H,dv]; beta [B,H]; S [B,H,dk,dv].
+ * Each state element is read once and written once.
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           float* S, void* o,
+                           int B, int H, int dk, int dv,
+                           kda_dtype dtype, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* kda_status_string(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_22_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return kda.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert set(syms) == {"kda_prefill_workspace_size", "kda_prefill_fwd",
+                         "kda_decode_step", "kda_status_string"}
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, 99):
+        assert kda.kda_status_string(code)
+    assert kda.kda_status_string(OK) == "ok"
+
+
+# Fake, 256-byte-spaced device addresses: validation must reject before any use.
+BASE = 1 << 40
+
+
+def P(i, off=0):
+    return ctypes.c_void_p(BASE + (i << 30) + off)
+
+
+def prefill(lib, *, q=P(0), k=P(1), v=P(2), la=P(3), beta=P(4), S0=P(5), o=P(6), Sf=P(7),
+            B=1, T=64, H=2, dk=128, dv=128, dt=1, chunk=64, ws=None, ws_bytes=0):
+    return lib.kda_prefill_fwd(q, k, v, la, beta, S0, o, Sf, B, T, H, dk, dv, dt, chunk,
+                               ws, ws_bytes, None)
+
+
+def decode(lib, *, q=P(0), k=P(1), v=P(2), la=P(3), beta=P(4), S=P(5), o=P(6),
+           B=2, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_decode_step(q, k, v, la, beta, S, o, B, H, dk, dv, dt, None)
+
+
+def test_prefill_rejects(lib):
+    assert prefill(lib, B=-1) == INVALID
+    assert prefill(lib, T=-5) == INVALID
+    assert prefill(lib, H=-1) == INVALID
+    assert prefill(lib, dk=48) == UNSUPPORTED
+    assert prefill(lib, dv=256) == UNSUPPORTED
+    assert prefill(lib, chunk=128) == UNSUPPORTED
+    assert prefill(lib, chunk=8) == UNSUPPORTED
+    assert prefill(lib, dt=7) == UNSUPPORTED
+    for name in ("q", "k", "v", "la", "beta", "o"):
+        assert prefill(lib, **{name: None}) == INVALID, name
+    for name in ("q", "k", "v", "la", "beta", "S0", "o", "Sf"):
+        assert prefill(lib, **{name: P(8, 4)}) == INVALID, name   # misaligned
+    # o overlapping an input, S_final overlapping an input other than S0
+    assert prefill(lib, o=P(0, 256)) == INVALID
+    assert prefill(lib, Sf=P(2, 1024)) == INVALID
+    assert prefill(lib, Sf=P(5, 256)) == INVALID     # partial overlap with S0
+    assert prefill(lib, o=P(7)) == INVALID           # o overlapping S_final
+
+
+def test_prefill_empty_batch_is_noop(lib):
+    # nothing to do: returns before touching the device
+    assert prefill(lib, B=0) == OK
+    assert prefill(lib, H=0, q=None, k=None) == OK
+
+
+def test_workspace_query(lib):
+    assert lib.kda_prefill_workspace_size(8, 8192, 32, 128, 128, 1, 64) == 0
+
+
+def test_decode_rejects(lib):
+    assert decode(lib, B=-1) == INVALID
+    assert decode(lib, dk=24) == UNSUPPORTED
+    assert decode(lib, dt=3) == UNSUPPORTED
+    for name in ("q", "k", "v", "la", "beta", "S", "o"):
+        assert decode(lib, **{name: None}) == INVALID, name
+        assert decode(lib, **{name: P(9, 8)}) == INVALID, name
+    assert decode(lib, o=P(5, 512)) == INVALID       # o inside S
+    assert decode(lib, S=P(1, 64)) == INVALID        # S overlapping k
+    assert decode(lib, B=0) == OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.kda_prefill_fwd(x, x, x, x, torch.zeros(1, 4, 1))

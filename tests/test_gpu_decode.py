@@ -1,0 +1,85 @@
+"""GPU parity of kda_decode_step (through the C ABI) against the fp64 oracle."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_22_amd as kda
+import oracle
+import workloads as W
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, report, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def rand_step(B, H, dk, dv, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    unit = lambda x: x / x.norm(dim=-1, keepdim=True)
+    return dict(q=unit(torch.randn(B, H, dk, generator=g)).to(dtype),
+                k=unit(torch.randn(B, H, dk, generator=g)).to(dtype),
+                v=torch.randn(B, H, dv, generator=g).to(dtype),
+                log_alpha=-0.001 - 0.099 * torch.rand(B, H, dk, generator=g),
+                beta=torch.sigmoid(torch.randn(B, H, generator=g)))
+
+
+@pytest.mark.parametrize("dk,dv", list(itertools.product([16, 32, 64, 128], repeat=2)))
+def test_decode_fp32_all_shapes(dk, dv):
+    s = rand_step(3, 5, dk, dv, torch.float32, dk * 1000 + dv)
+    S0 = 0.3 * torch.randn(3, 5, dk, dv, generator=torch.Generator().manual_seed(1))
+    Sd = S0.to(DEV)
+    od = kda.kda_decode_step(**to_dev(s), S=Sd)
+    torch.cuda.synchronize()
+    ro, rS = oracle.decode_f64(s["q"], s["k"], s["v"], s["log_alpha"], s["beta"], S0)
+    report(f"decode fp32 dk{dk} dv{dv}", [("o", od, ro), ("S", Sd, rS)], TOL_F32)
+
+
+def test_decode_bf16_multi_step():
+    B, H, D = 8, 32, 128
+    S0 = 0.02 * torch.randn(B, H, D, D, generator=torch.Generator().manual_seed(2))
+    Sd = S0.to(DEV)
+    S = S0.double().numpy()
+    outs, refs = [], []
+    for step in range(16):
+        s = rand_step(B, H, D, D, torch.bfloat16, 100 + step)
+        outs.append(kda.kda_decode_step(**to_dev(s), S=Sd).cpu())
+        ro, S = oracle.decode_f64(s["q"], s["k"], s["v"], s["log_alpha"], s["beta"], S)
+        refs.append(ro)
+    torch.cuda.synchronize()
+    report("decode bf16 B8 H32 D128, 16 steps", [("o", torch.stack(outs), np.stack(refs)),
+                                                ("S", Sd, S)], TOL_BF16)
+
+
+def test_decode_config_full():
+    """B=256, H=32, 1024 steps at full size; every head checked on the first
+    step, sampled heads over all 1024 steps (outputs stacked) and at the end."""
+    c = W.DECODE_CONFIGS["decode"]
+    S = W.decode_state(c, device=DEV)
+    S_init = S.cpu()
+    picks = [(0, 0), (17, 5), (100, 31), (255, 12), (128, 20), (63, 7)]
+    bi = torch.tensor([p[0] for p in picks], device=DEV)
+    hi = torch.tensor([p[1] for p in picks], device=DEV)
+    sub_in = {n: [] for n in ("q", "k", "v", "log_alpha", "beta")}
+    sub_out = []
+    for step in range(c.steps):
+        s = W.decode_step_inputs(c, step, device=DEV)
+        if step == 0:
+            s0_host = {n: t.cpu() for n, t in s.items()}
+        o = kda.kda_decode_step(s["q"], s["k"], s["v"], s["log_alpha"], s["beta"], S)
+        if step == 0:
+            torch.cuda.synchronize()
+            ro, rS = oracle.decode_f64(s0_host["q"], s0_host["k"], s0_host["v"],
+                                       s0_host["log_alpha"], s0_host["beta"], S_init)
+            report("decode config step 0, all 8192 heads", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+        for n in sub_in:
+            sub_in[n].append(s[n][bi, hi])
+        sub_out.append(o[bi, hi])
+    torch.cuda.synchronize()
+    # sampled heads as 6 independent sequences of 1024 tokens: [1, steps, 6, ...]
+    seq = {n: torch.stack(v, 0).unsqueeze(0).cpu() for n, v in sub_in.items()}
+    S0s = S_init[[p[0] for p in picks], [p[1] for p in picks]].unsqueeze(0)
+    ro, rS = oracle.prefill_f64(seq["q"], seq["k"], seq["v"], seq["log_alpha"], seq["beta"], S0s)
+    got_o = torch.stack(sub_out, 0).unsqueeze(0)
+    got_S = S[bi, hi].unsqueeze(0)
+    report("decode config 1024 steps, sampled heads", [("o", got_o, ro), ("S", got_S, rS)],
+           TOL_BF16)

@@ -1,0 +1,233 @@
+"""GPU parity of kda_prefill_fwd (through the C ABI) against the fp64 oracle.
+
+Small cases are compared element by element over whole tensors; the large
+configurations run at full size in the launch configuration the benchmark
+times, and are compared on sampled heads the oracle can afford.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_22_amd as kda
+import oracle
+import workloads as W
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, report, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prefill(xd, chunk=64, S0="x", **kw):
+    s0 = xd["S0"] if isinstance(S0, str) else S0
+    o, S = kda.kda_prefill_fwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], s0,
+                               chunk=chunk, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def oracle_prefill(x, S0="x"):
+    s0 = x["S0"] if isinstance(S0, str) else S0
+    return oracle.prefill_f64(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], s0)
+
+
+def test_cpu_sized_config_fp32():
+    c = W.PREFILL_CONFIGS["cpu"]
+    x = W.prefill_inputs(c)
+    o, S = gpu_prefill(to_dev(x), chunk=c.chunk)
+    ro, rS = oracle_prefill(x)
+    report("cpu config fp32 B1 H2 T64 D16 C16", [("o", o, ro), ("S", S, rS)], TOL_F32)
+
+
+@pytest.mark.parametrize("dk,dv,T,chunk", [(16, 16, 64, 16), (32, 64, 100, 32),
+                                           (64, 32, 77, 64), (128, 128, 40, 64),
+                                           (16, 128, 130, 16), (128, 16, 33, 32)])
+def test_fp32_shapes_ragged(dk, dv, T, chunk):
+    c = W.PREFILL_CONFIGS["batched"]
+    import dataclasses
+    c = dataclasses.replace(c, dk=dk, dv=dv)
+    x = W.prefill_inputs(c, B=2, T=T, H=3, dtype=torch.float32)
+    o, S = gpu_prefill(to_dev(x), chunk=chunk)
+    ro, rS = oracle_prefill(x)
+    report(f"fp32 dk{dk} dv{dv} T{T} C{chunk}", [("o", o, ro), ("S", S, rS)], TOL_F32)
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 200, 256])
+def test_bf16_mfma_small(T):
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=2, T=T, H=3)
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report(f"bf16 B2 H3 T{T} D128 C64 with S0", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_bf16_prefill_config_full():
+    c = W.PREFILL_CONFIGS["prefill"]
+    x = W.prefill_inputs(c)
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report("prefill config B1 H16 T4096 D128 (all heads)", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_bf16_batched_config_sampled():
+    c = W.PREFILL_CONFIGS["batched"]
+    xd = W.prefill_inputs(c, device=DEV)
+    o, S = gpu_prefill(xd)
+    picks = [(0, 0), (1, 7), (3, 31), (4, 16), (6, 3), (7, 30)]
+    for b, h in picks:
+        sub = {n: (t[b:b + 1, :, h:h + 1].cpu() if n not in ("S0",) else t[b:b + 1, h:h + 1].cpu())
+               for n, t in xd.items()}
+        ro, rS = oracle.prefill_f64(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"],
+                                    sub["S0"])
+        report(f"batched config B8 H32 T8192 head (b={b}, h={h})",
+               [("o", o[b:b + 1, :, h:h + 1], ro), ("S", S[b:b + 1, h:h + 1], rS)], TOL_BF16)
+
+
+def test_bf16_long_config_sampled():
+    """1M-token context at full size. Sampled heads are checked on the first
+    65536 tokens exactly, and on the last 65536 tokens from a zero state: the
+    state entering that window is damped by the product over the window of the
+    largest per-step decay, which the test computes and requires to be
+    negligible against the tolerance."""
+    c = W.PREFILL_CONFIGS["long"]
+    T, H, D = c.T, c.H, c.dk
+    q = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    la = torch.empty((1, T, H, D), dtype=torch.float32, device=DEV)
+    beta = torch.empty((1, T, H), dtype=torch.float32, device=DEV)
+    for h in range(H):
+        xh = W.prefill_inputs_per_head(c, h, device=DEV)
+        q[:, :, h] = xh["q"][:, :, 0]
+        k[:, :, h] = xh["k"][:, :, 0]
+        v[:, :, h] = xh["v"][:, :, 0]
+        la[:, :, h] = xh["log_alpha"][:, :, 0]
+        beta[:, :, h] = xh["beta"][:, :, 0]
+        del xh
+    o, S = kda.kda_prefill_fwd(q, k, v, la, beta, None)
+    torch.cuda.synchronize()
+    Wn = 65536
+    for h in (0, 21):
+        head = lambda t, sl: t[:, sl, h:h + 1].cpu()
+        first = slice(0, Wn)
+        ro, _ = oracle.prefill_f64(head(q, first), head(k, first), head(v, first),
+                                   head(la, first), head(beta, first), None)
+        report(f"long config first {Wn} tokens, head {h}", [("o", o[:, first, h:h + 1], ro)],
+               TOL_BF16)
+        last = slice(T - Wn, T)
+        damp = float(torch.exp(la[0, last, h].double().max(dim=-1).values.sum()))
+        assert damp < 1e-6, damp
+        ro, rS = oracle.prefill_f64(head(q, last), head(k, last), head(v, last),
+                                    head(la, last), head(beta, last), None)
+        report(f"long config last {Wn} tokens + final state, head {h} (damping {damp:.1e})",
+               [("o", o[:, last, h:h + 1], ro), ("S", S[:, h:h + 1], rS)], TOL_BF16)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_size_changes_nothing(chunk):
+    c = W.PREFILL_CONFIGS["prefill"]
+    x = W.prefill_inputs(c, B=1, T=150, H=2)
+    o, S = gpu_prefill(to_dev(x), chunk=chunk)
+    ro, rS = oracle_prefill(x)
+    report(f"bf16 chunk {chunk} T150", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_split_sequence_continuation():
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=1, T=320, H=4)
+    xd = to_dev(x)
+    cut = lambda d, sl: {n: (t[:, sl] if n != "S0" else t) for n, t in d.items()}
+    oa, Sa = gpu_prefill(cut(xd, slice(0, 128)))
+    ob, Sb = gpu_prefill(cut(xd, slice(128, 320)), S0=Sa)
+    o, S = gpu_prefill(xd)
+    ro, rS = oracle_prefill(x)
+    report("split 128+192 vs oracle", [("o", torch.cat([oa, ob], 1), ro), ("S", Sb, rS)], TOL_BF16)
+    report("split vs one shot", [("S", Sb, S.cpu().double().numpy())], 5e-3)
+
+
+def test_state_in_place():
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=1, T=130, H=2)
+    xd = to_dev(x)
+    S = xd["S0"].clone()
+    o, Sf = gpu_prefill(xd, S0=S, S_final=S)
+    assert Sf.data_ptr() == S.data_ptr()
+    ro, rS = oracle_prefill(x)
+    report("in-place S_final = S0", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_empty_sequence_copies_state():
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=2, T=0, H=3)
+    xd = to_dev(x)
+    o, S = gpu_prefill(xd)
+    assert o.shape == (2, 0, 3, 128)
+    assert torch.equal(S, xd["S0"])
+    o, S = gpu_prefill(xd, S0=None)
+    assert torch.count_nonzero(S) == 0
+
+
+def test_no_decay_no_write_keeps_state_exactly():
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=1, T=190, H=2)
+    x["beta"].zero_()
+    x["log_alpha"].zero_()
+    xd = to_dev(x)
+    o, S = gpu_prefill(xd)
+    assert torch.equal(S, xd["S0"])
+    ro, _ = oracle_prefill(x)
+    report("beta=0, alpha=1: o = S0^T q", [("o", o, ro)], TOL_BF16)
+
+
+def test_strong_decay_at_bound():
+    # log-decay in [-5, -4]: the lower end of the supported range
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=1, T=192, H=2)
+    x["log_alpha"] = -4.0 - torch.rand(x["log_alpha"].shape, generator=torch.Generator().manual_seed(1))
+    o, S = gpu_prefill(to_dev(x))
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    ro, rS = oracle_prefill(x)
+    report("log-decay in [-5,-4]", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_basis_keys_store_and_retrieve():
+    # alpha = 1, beta = 1, S0 = 0, keys are signed basis vectors (exact in bf16):
+    # the final state maps every key back to its value.
+    T, D = 128, 128
+    g = torch.Generator().manual_seed(3)
+    perm = torch.randperm(D, generator=g)
+    sign = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
+    keys = torch.zeros(T, D)
+    keys[torch.arange(T), perm] = sign
+    vals = torch.randn(T, D, generator=g)
+    x = dict(q=keys.view(1, T, 1, D).bfloat16(), k=keys.view(1, T, 1, D).bfloat16(),
+             v=vals.view(1, T, 1, D).bfloat16(), log_alpha=torch.zeros(1, T, 1, D),
+             beta=torch.ones(1, T, 1), S0=None)
+    o, S = gpu_prefill(to_dev(x))
+    retrieved = keys @ S[0, 0].cpu()
+    report("basis keys: k_i^T S = v_i", [("retrieved", retrieved, x["v"][0, :, 0].double().numpy())],
+           TOL_BF16)
+    ro, rS = oracle_prefill(x)
+    report("basis keys vs oracle", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_prefill_of_one_token_is_a_decode_step():
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=2, T=1, H=4)
+    xd = to_dev(x)
+    o, S = gpu_prefill(xd)
+    Sd = xd["S0"].clone()
+    od = kda.kda_decode_step(xd["q"][:, 0].contiguous(), xd["k"][:, 0].contiguous(),
+                             xd["v"][:, 0].contiguous(), xd["log_alpha"][:, 0].contiguous(),
+                             xd["beta"][:, 0].contiguous(), Sd)
+    torch.cuda.synchronize()
+    report("T=1 prefill vs decode", [("o", o[:, 0], od.cpu().double().numpy()),
+                                     ("S", S, Sd.cpu().double().numpy())], TOL_BF16)
+
+
+def test_deterministic():
+    c = W.PREFILL_CONFIGS["batched"]
+    xd = to_dev(W.prefill_inputs(c, B=2, T=300, H=4))
+    o1, S1 = gpu_prefill(xd)
+    o2, S2 = gpu_prefill(xd)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)

@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""KDA prefill / decode throughput on one MI355X.
+
+One JSON line on stdout. The headline (``value``) is prefill tokens/s on the
+workload chosen with --workload (default: B=1, H=16, T=4096, d=128, chunk 64,
+bf16 q/k/v, fp32 state). A "step" is one full prefill of that batch (one
+launch of the fused kernel: chunk cumsum and decay scaling, intra-chunk Gram,
+UT inverse, pseudo-values, outputs and the state carry). Inputs are resident
+in HBM before timing; each timed step reads its own replica of the batch so
+the 256 MB last-level cache cannot hold the inputs between steps.
+
+Also reported in the same line: the decode workload (B=256, H=32, d=128, 1024
+sequential steps, fp32 state of 537 MB streamed per step) as "decode", the
+roofline of the dominant kernel timed with HIP events on its stream, and the
+fp64 CPU oracle timed on the host cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+LLC_BYTES = 256 << 20           # Infinity Cache
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_22_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[f"{kernel}|{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bench_prefill(cfg, steps, warmup):
+    import torch
+    import gated_delta_rule_22_amd as kda
+    import workloads as W
+    from workloads import accounting as A
+
+    dev = torch.device("cuda:0")
+    x = W.prefill_inputs(cfg, device=dev)
+    per_batch = sum(t.numel() * t.element_size() for t in x.values() if t is not None)
+    reps = max(1, min(steps + warmup, math.ceil(2 * LLC_BYTES / per_batch)))
+    batches = [x] + [{n: (t.clone() if t is not None else None) for n, t in x.items()}
+                     for _ in range(reps - 1)]
+    outs = [(torch.empty_like(b["v"]),
+             torch.empty((cfg.B, cfg.H, cfg.dk, cfg.dv), dtype=torch.float32, device=dev))
+            for b in batches]
+
+    ws_bytes = kda.kda_prefill_workspace_size(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, cfg.dtype,
+                                              cfg.chunk)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        b = batches[i % reps]
+        o, S = outs[i % reps]
+        kda.kda_prefill_fwd(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], b["S0"],
+                            chunk=cfg.chunk, o=o, S_final=S, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    tokens = cfg.B * cfg.T
+    flops = A.prefill_flops(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.chunk)
+    flops_c = A.prefill_flops_conservative(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.chunk)
+    nbytes = A.prefill_bytes(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, elt=2,
+                             has_s0=cfg.s0_std > 0, writes_state=True)
+    t = kern_ms * 1e-3
+    return dict(wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=kern_ms,
+                tokens_per_s=tokens * steps / wall, flops=flops, flops_cons=flops_c,
+                bytes=nbytes, gbs=nbytes / t / 1e9, tflops=flops / t / 1e12,
+                tflops_cons=flops_c / t / 1e12, replicas=reps, workspace_bytes=ws_bytes)
+
+
+def bench_decode(cfg, loops=2):
+    import torch
+    import gated_delta_rule_22_amd as kda
+    import workloads as W
+    from workloads import accounting as A
+
+    dev = torch.device("cuda:0")
+    S0 = W.decode_state(cfg, device=dev)
+    S = torch.empty_like(S0)
+    steps = [W.decode_step_inputs(cfg, s, device=dev) for s in range(cfg.steps)]
+    o = torch.empty((cfg.B, cfg.H, cfg.dv), dtype=cfg.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(events=None):
+        for i, s in enumerate(steps):
+            if events is not None:
+                events[i][0].record(stream)
+            kda.kda_decode_step(s["q"], s["k"], s["v"], s["log_alpha"], s["beta"], S, o=o)
+            if events is not None:
+                events[i][1].record(stream)
+
+    S.copy_(S0)
+    run()  # warm-up pass
+    best = None
+    for _ in range(loops):
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(cfg.steps)]
+        t0 = time.perf_counter()
+        run(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = sum(a.elapsed_time(b) for a, b in ev) / cfg.steps
+        if best is None or wall < best[0]:
+            best = (wall, kern_ms)
+    wall, kern_ms = best
+    nbytes = A.decode_step_bytes(cfg.B, cfg.H, cfg.dk, cfg.dv)
+    return dict(steps=cfg.steps, wall_s=wall, steps_per_s=cfg.steps / wall,
+                tokens_per_s=cfg.B * cfg.steps / wall, kernel_us=kern_ms * 1e3,
+                bytes_per_step=nbytes, gbs=nbytes / (kern_ms * 1e-3) / 1e9,
+                flops_per_step=A.decode_step_flops(cfg.B, cfg.H, cfg.dk, cfg.dv))
+
+
+def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18):
+    """fp64 oracle on the host cores over a bounded sample of the same
+    workload: whole heads (one per thread) over the first tokens of the
+    sequence. Inputs are converted before the clock starts."""
+    import oracle
+    import workloads as W
+
+    heads = min(cfg.H, max_heads)
+    T = min(cfg.T, max_tokens)
+    xs = [W.prefill_inputs_per_head(cfg, h, T=T) for h in range(heads)]
+    f64 = lambda key: np.ascontiguousarray(
+        np.concatenate([x[key].double().numpy() for x in xs], axis=2))
+    q, k, v, la, beta = (f64(n) for n in ("q", "k", "v", "log_alpha", "beta"))
+    S0 = None
+    if xs[0]["S0"] is not None:
+        S0 = np.ascontiguousarray(np.concatenate([x["S0"].double().numpy() for x in xs], axis=1))
+    threads = min(os.cpu_count() or 1, heads)
+    t0 = time.perf_counter()
+    oracle.prefill_f64(q, k, v, la, beta, S0, nthreads=threads)
+    dt = time.perf_counter() - t0
+    # token-heads per second over the sample, as tokens/s of the full workload
+    tps = heads * T / dt / cfg.H
+    return dict(value=tps, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{heads} of {cfg.H} heads x first {T} of {cfg.T} tokens (B=1), "
+                       f"fp64 token loop, {dt:.2f} s on {threads} threads; "
+                       f"rate scaled to {cfg.H} heads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "batched", "long"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the KDA path here "
+              "has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_22_amd as kda
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kda.load_library()
+    cfg = W.PREFILL_CONFIGS[args.workload]
+    steps = args.steps
+    if args.workload == "long":
+        steps = min(steps, 5)
+    _log(f"[bench] prefill {cfg.describe()}: warmup {args.warmup}, steps {steps}")
+    pre = bench_prefill(cfg, steps, args.warmup)
+    _log(f"[bench] prefill kernel {pre['kernel_ms'] * 1e3:.1f} us, {pre['gbs']:.0f} GB/s, "
+         f"{pre['tflops']:.1f} TFLOP/s")
+
+    workload = cfg.describe()
+    traffic = measured_traffic("prefill_mfma", workload)
+    result = {
+        "metric": "KDA prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW",
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "B": cfg.B, "T": cfg.T, "H": cfg.H, "dk": cfg.dk,
+                   "dv": cfg.dv, "chunk": cfg.chunk, "state": "fp32",
+                   "input_replicas": pre["replicas"], "workspace_bytes": pre["workspace_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": pre["gbs"] / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "prefill_mfma_kernel",
+                     "kernel_us": pre["kernel_ms"] * 1e3, "algorithmic_bytes": pre["bytes"]},
+        "mfma": {"flops_per_step": pre["flops"], "achieved_tflops": pre["tflops"],
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": pre["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                 "frac_without_inverse": pre["tflops_cons"] / MFMA_BF16_PEAK_TFLOPS},
+    }
+
+    if not args.no_decode:
+        dc = W.DECODE_CONFIGS["decode"]
+        _log(f"[bench] decode {dc.describe()}")
+        dec = bench_decode(dc)
+        _log(f"[bench] decode {dec['kernel_us']:.1f} us/step, {dec['gbs']:.0f} GB/s")
+        result["decode"] = {
+            "workload": dc.describe(), "steps_per_s": dec["steps_per_s"],
+            "tokens_per_s": dec["tokens_per_s"], "us_per_step": dec["wall_s"] / dec["steps"] * 1e6,
+            "roofline": {"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": dec["gbs"] / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode", dc.describe()),
+                         "kernel": "decode_kernel", "kernel_us": dec["kernel_us"],
+                         "algorithmic_bytes": dec["bytes_per_step"]},
+        }
+
+    if not args.no_cpu:
+        _log("[bench] cpu oracle baseline")
+        result["cpu_baseline"] = cpu_baseline_prefill(cfg, max_heads=os.cpu_count() or 1)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,8 +48,9 @@ const char* kda_status_string(kda_status s) {
 
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dtype,
                                   int chunk) {
-    (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)dtype; (void)chunk;
-    return 0;  // the fused kernels keep every intermediate on chip
+    if (B <= 0 || T <= 0 || H <= 0 || dtype != KDA_BF16) return 0;
+    if (!kda::prefill_mfma_supported(dk, dv, chunk)) return 0;
+    return kda::prefill_mfma_workspace(B, T, H);
 }
 
 kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
@@ -61,9 +62,6 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
-    if (ws_bytes < kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk))
-        return KDA_ERR_WORKSPACE;
-    (void)ws;
     if (B == 0 || H == 0) return KDA_OK;
 
     const size_t elt = dtype == KDA_BF16 ? 2 : 4;
@@ -80,6 +78,9 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
     const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_final};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk);
+    if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need)) return KDA_ERR_WORKSPACE;
+    if (ws_need > 0 && !aligned16(ws)) return KDA_ERR_INVALID_ARG;
 
     const Range rq(q, T ? nk * elt : 0), rk(k, T ? nk * elt : 0), rv(v, T ? nv * elt : 0);
     const Range rla(log_alpha, T ? nk * 4 : 0), rb(beta, T ? tok * 4 : 0);
@@ -93,11 +94,17 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
             return KDA_ERR_INVALID_ARG;
         }
     if (overlap(ro, rsf)) return KDA_ERR_INVALID_ARG;
+    if (ws_need > 0) {
+        const Range rws(ws, ws_need);
+        for (const Range& in : inputs)
+            if (overlap(rws, in)) return KDA_ERR_INVALID_ARG;
+        if (overlap(rws, ro) || overlap(rws, rsf)) return KDA_ERR_INVALID_ARG;
+    }
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
-        e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, st);
+        e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, ws, st);
     else
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
                                         S_final, B, T, H, dk, dv, chunk ? chunk : 64, st);

@@ -63,6 +63,13 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // Natural exponential through the hardware exp2 (v_exp_f32).
 __device__ __forceinline__ float exp_e(float x) { return __expf(x); }
 
+// Workgroup barrier for LDS hazards only: waits for this wave's LDS (and
+// scalar) operations, not for outstanding global loads, so register
+// prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Wait until this wave's LDS operations have completed.
 __device__ __forceinline__ void lds_fence_wave() {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)

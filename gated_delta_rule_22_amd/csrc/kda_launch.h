@@ -17,11 +17,13 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
                                   void* o, float* S_final, int B, int T, int H, int dk,
                                   int dv, int chunk, hipStream_t st);
 
-// bf16 MFMA chunked prefill for dk = dv = 128, chunk 64. Returns
-// hipErrorInvalidValue if the shape is not one it implements.
+// bf16 MFMA chunked prefill for dk = dv = 128, chunk 64. For few heads it
+// runs a chunk-parallel prep kernel and a state kernel that communicate
+// through `ws` (prefill_mfma_workspace() bytes); otherwise one fused kernel.
 bool prefill_mfma_supported(int dk, int dv, int chunk);
+size_t prefill_mfma_workspace(int B, int T, int H);
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
                                const float* beta, const float* S0, void* o, float* S_final,
-                               int B, int T, int H, hipStream_t st);
+                               int B, int T, int H, void* ws, hipStream_t st);
 
 }  // namespace kda

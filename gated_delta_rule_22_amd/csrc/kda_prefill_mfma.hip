@@ -1,33 +1,41 @@
-// Fused chunk-parallel KDA prefill, bf16 MFMA contractions with fp32 state.
+// Chunk-parallel KDA prefill for dk = dv = 128, chunk 64: bf16 MFMA
+// contractions, fp32 state.
 //
-// Method ("Kimi K3: the manos...", section "FlashKDA Algorithm"): the
-// sequence is cut into chunks of C = 64 tokens. Inside a chunk with starting
-// state S_in,
-//   B      = Diag(beta)(V - K_decay S_in),  L = StrictTril(Diag(beta) K_decay K_inv^T)
-//   U      = (I + L)^{-1} B                   (UT transform, pseudo-values)
-//   O      = Q_decay S_in + M_qk U,           M_qk = tril(Q_decay K_inv^T)
-//   S_out  = Diag(a_last) S_in + K_restore^T U
-// with a_t the inclusive cumulative decay from the chunk start.
+// Method ("Kimi K3: the manos...", section "FlashKDA Algorithm"): inside a
+// chunk of C = 64 tokens with starting state S_in,
+//   U     = (I + L)^{-1} Diag(beta)(V - K_decay S_in),  L = StrictTril(Diag(beta) K_decay K_inv^T)
+//   O     = Q_decay S_in + M_qk U,                      M_qk = tril(Q_decay K_inv^T)
+//   S_out = Diag(a_last) S_in + K_restore^T U
+// a_t being the inclusive cumulative decay from the chunk start.
 //
-// MI355X design (one workgroup per (batch, head, value block of DVB columns),
-// the whole sequence processed in order, state never leaves the chip):
-//  * The state block S (128 x DVB fp32) lives in MFMA accumulator registers:
-//    wave w owns value columns [16w, 16w+16) and all 128 key rows, as eight
-//    16x16 tiles. It feeds MFMAs directly as the B operand (the K index of a
-//    32-deep step is permuted identically on both operands, so the
-//    accumulator layout needs no LDS round trip).
-//  * U does not depend on S_in except linearly: U = U0 - W S_in with
-//    U0 = INV Diag(beta) V and W = INV Diag(beta) K_decay. U0 and W are
-//    formed by blocked forward substitution on 16-token blocks (fp32 inverses
-//    of the four 16x16 diagonal blocks, bf16 MFMA for the rest), so the
-//    state-dependent chain per chunk is three MFMA passes: U, then O and S.
-//  * Decay factors never overflow: the Gram matrices are built per 16x16
-//    token block, factoring the decay at a block boundary so that every
-//    factor is <= 1 except the within-block inverse decay, which is bounded by
-//    exp(5 * 16) for log-decays in [-5, 0] (the bound stated on the
-//    trillion-scale architecture page, section 4) and fits fp32/bf16 range.
-//  * The next chunk's q, k, log-decay, v and beta are loaded into registers
-//    while the current chunk computes.
+// Restated for the MI355X (every step below is exact algebra of the above):
+//  * U is affine in S_in: U = U0 - W S_in with U0 = INV Diag(beta) V and
+//    W = INV Diag(beta) K_decay, INV = (I + L)^{-1}. U0 and W are built by
+//    forward substitution over four 16-token blocks (fp32 inverses of the
+//    16x16 diagonal blocks, bf16 MFMA elsewhere). Only three MFMA passes then
+//    depend on the state: U, then O and S_out.
+//  * Decay factors never overflow. With b_t the decay accumulated from the
+//    start of t's 16-token block to t, the Gram entry for t in block I and s
+//    in block J <= I is  sum_d (k_t b_t)[d] (k_s / b_s)[d] G_IJ[d],  G_IJ the
+//    decay over blocks J..I-1 (1 on the diagonal). Every factor is <= 1
+//    except 1/b_s <= exp(80) for log-decays in [-5, 0] (the bound on the
+//    trillion-scale architecture page, section 4), inside fp32/bf16 range.
+//    K_decay, Q_decay and K_restore are likewise products of factors <= 1.
+//
+// Kernels:
+//  * fused_kernel: one workgroup per (batch*head, 16*NW value columns); walks
+//    the whole sequence. The state block lives in MFMA accumulators (wave w
+//    owns 16 columns x 128 rows) and feeds the next chunk's MFMAs directly as
+//    the B operand: the K index of each 32-deep step is permuted identically
+//    on both operands, so no LDS round trip is needed. The next chunk's
+//    inputs are loaded into registers while the current one computes.
+//  * prep_kernel + state_kernel: for few heads. The prep kernel runs the
+//    state-independent work of many chunks in parallel and writes, per
+//    chunk-head, -W, Q_decay, K_restore^T, M_qk (bf16, in the padded layout
+//    the state kernel keeps in LDS), U0 and a_last to a workspace. The state
+//    kernel then walks the chunks in order doing only the three state
+//    passes (one wave per 16 value columns), streaming each chunk's operands
+//    into LDS with direct global-to-LDS loads one chunk ahead.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -36,32 +44,49 @@ namespace mf {
 
 constexpr int DK = 128;
 constexpr int C = 64;
-constexpr int KS = 136;   // padded row stride (bf16) of [64][128] tiles
-constexpr int TS = 72;    // padded row stride (bf16) of [*][64] tiles
-constexpr int LDS_ = 16 * 16 + 4;  // fp32 diagonal block stride
+constexpr int KS = 136;            // padded row stride (bf16) of [64][128] tiles
+constexpr int TS = 72;             // padded row stride (bf16) of [*][64] tiles
+constexpr int LDT = 16 * 16 + 4;   // fp32 stride of one transposed diagonal L block
 
-template <int DVB>
-struct Smem {
-    static constexpr int VS = DVB + 8;
-    bf16 Kd[C * KS];        // k_t * exp(c_t - c_{blockstart-1}): Gram left (L)
-    bf16 Qd[C * KS];        // q_t * same: Gram left (M_qk)
-    bf16 Ki[C * KS];        // k_s * exp(c_{blockstart-1} - c_s): diagonal-block right; later -W
-    bf16 Ke[96 * KS];       // k_s * exp(c_{blockend} - c_s), blocks 0..2 + gap copies; later Q_decay
-    bf16 KrT[DK * TS];      // K_restore^T [channel][token]
-    bf16 V[C * VS];         // this workgroup's value columns
-    bf16 nL[C * TS];        // -L (strictly lower; upper blocks stay zero)
-    bf16 M[C * TS];         // M_qk (lower incl. diagonal; upper blocks stay zero)
-    float Ld[4 * LDS_];     // diagonal blocks of L, fp32
-    bf16 D[4 * 256];        // (I + L_II)^{-1}, bf16
-    float P[4 * DK];        // exp(c_{blockstart-1}) per block, channel
-    float Tot[4 * DK];      // per-block sums of log-decay
-    float alast[DK];        // exp(c_63)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Per-chunk operands prepared in LDS.
+struct Prep {
+    bf16 Kd[C * KS];     // k_t b_t                  Gram left (L), K_decay = Kd * P
+    bf16 Qd[C * KS];     // q_t b_t                  Gram left (M); then Q_decay in place
+    bf16 Ki[C * KS];     // k_s / b_s                Gram right; then -W in place
+    bf16 KrT[DK * TS];   // K_restore^T [channel][token]
+    bf16 RkT[DK * TS];   // (Diag(beta) K_decay)^T [channel][token]: substitution input
+    bf16 nL[C * TS];     // -L (upper blocks stay zero)
+    bf16 M[C * TS];      // M_qk (upper blocks stay zero)
+    float LdT[4 * LDT];  // diagonal blocks of L, fp32, transposed [s][t]
+    bf16 D[4 * 256];     // (I + L_II)^{-1}
+    float P[4 * DK];     // decay from the chunk start to the start of block I
+    float G[6 * DK];     // decay over blocks J..I-1 for the 6 pairs J < I
+    float alast[DK];     // decay over the whole chunk
+    float Tot[8 * DK];   // log-decay sums of the 8-or-4 token ranges
     float beta[C];
 };
 
-// Gram products: 10 lower block pairs (I, J) x {KK, QK}.
-__constant__ int kPairI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kPairJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// Operand record written by the prep kernel, read by the state kernel.
+// Offsets in bytes; the first five regions are copied verbatim into LDS.
+constexpr int REC_NW = 0;
+constexpr int REC_QD = REC_NW + C * KS * 2;
+constexpr int REC_KR = REC_QD + C * KS * 2;
+constexpr int REC_M = REC_KR + DK * TS * 2;
+constexpr int REC_AL = REC_M + C * TS * 2;
+constexpr int REC_LDS = REC_AL + DK * 4;          // bytes staged into LDS per chunk
+constexpr int REC_U0 = REC_LDS;                   // U0, bf16, MFMA accumulator-tile order
+constexpr int REC_BYTES = REC_U0 + C * 128 * 2;
+static_assert(REC_LDS % 16 == 0 && REC_BYTES % 256 == 0, "record alignment");
+
+// The 10 lower block pairs (I, J), row-major, 2 bits per entry.
+constexpr uint32_t kPairI = (0u << 0) | (1u << 2) | (1u << 4) | (2u << 6) | (2u << 8) |
+                            (2u << 10) | (3u << 12) | (3u << 14) | (3u << 16) | (3u << 18);
+constexpr uint32_t kPairJ = (0u << 0) | (0u << 2) | (1u << 4) | (0u << 6) | (1u << 8) |
+                            (2u << 10) | (0u << 12) | (1u << 14) | (2u << 16) | (3u << 18);
 
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ s16x4 ld4(const bf16* p) { return *reinterpret_cast<const s16x4*>(p); }
@@ -75,333 +100,456 @@ __device__ __forceinline__ bf16x8 ldA_perm(const bf16* rowp, int k0, int g) {
 }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
-__device__ __forceinline__ float lo_bf(uint32_t u) { return bf16_from_bits((uint16_t)(u & 0xffffu)); }
-__device__ __forceinline__ float hi_bf(uint32_t u) { return bf16_from_bits((uint16_t)(u >> 16)); }
+__device__ __forceinline__ f32x2 unpack2(uint32_t u) {
+    return __builtin_convertvector(__builtin_bit_cast(bf16x2, u), f32x2);
+}
+
+// Multiply eight bf16 operand values by per-channel factors.
+__device__ __forceinline__ bf16x8 scale8(bf16x8 v, f32x4 g0, f32x4 g1) {
+    f32x8 f = __builtin_convertvector(v, f32x8);
+    f32x8 gg = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_convertvector(f * gg, bf16x8);
+}
+
+// ---------------------------------------------------------------------------
+// Chunk inputs held in registers between the load and the elementwise stage.
+template <int NW>
+struct Inputs {
+    static constexpr int TPT = C / NW;        // tokens per thread (16 or 8)
+    uint32_t k[TPT], q[TPT];                  // two channels, bf16 pair
+    f32x2 la[TPT];                            // two channels' log-decay
+    uint4 v[2];                               // two 16-byte pieces of the value block
+    float beta;
+};
+
+// Load chunk c's inputs. Thread (wave = token range, lane = channel pair).
+// Loads are unconditional (tail tokens re-read the last token) and the raw
+// values are kept as loaded: tail tokens are zeroed where they are consumed,
+// so no instruction waits on a load before the next chunk is needed.
+template <int NW, int DVB>
+__device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restrict__ q,
+                                            const bf16* __restrict__ k,
+                                            const bf16* __restrict__ v,
+                                            const float* __restrict__ log_alpha,
+                                            const float* __restrict__ beta, int b, int h, int T,
+                                            int H, int c, int col0)
+{
+    constexpr int TPT = C / NW;
+    constexpr int VPR = DVB / 8;   // 16-byte pieces per value row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = wave * TPT;
+    auto row = [&](int tok) -> size_t { return ((size_t)b * T + min(tok, T - 1)) * H + h; };
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+        const size_t base = row(c * C + t0 + j) * DK + 2 * lane;
+        in.k[j] = *reinterpret_cast<const uint32_t*>(k + base);
+        in.q[j] = *reinterpret_cast<const uint32_t*>(q + base);
+        in.la[j] = *reinterpret_cast<const f32x2*>(log_alpha + base);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int piece = tid + p * NW * 64;
+        const int t = piece / VPR, c8 = piece - t * VPR;
+        in.v[p] = *reinterpret_cast<const uint4*>(v + row(c * C + t) * 128 + col0 + 8 * c8);
+    }
+    if (tid < C) in.beta = beta[row(c * C + tid)];
+}
+
+// Stage 1a: per-range log-decay sums; values and beta to LDS. Tokens at or
+// past ntok are padding: zero decay, value and beta (exact, the recurrence
+// leaves the state unchanged for them).
+template <int NW, int DVB>
+__device__ __forceinline__ void stage1a(Prep& sm, bf16* sV, const Inputs<NW>& in, int ntok) {
+    constexpr int TPT = C / NW;
+    constexpr int VPR = DVB / 8;
+    constexpr int VS = DVB + 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = wave * TPT;
+    f32x2 sum = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) sum += (t0 + j < ntok) ? in.la[j] : f32x2{0.f, 0.f};
+    *reinterpret_cast<f32x2*>(&sm.Tot[wave * DK + 2 * lane]) = sum;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int piece = tid + p * NW * 64;
+        const int t = piece / VPR, c8 = piece - t * VPR;
+        *reinterpret_cast<uint4*>(&sV[t * VS + 8 * c8]) = (t < ntok) ? in.v[p] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (tid < C) sm.beta[tid] = (tid < ntok) ? in.beta : 0.f;
+}
+
+// Stage 1b: decay-scaled operands. Thread (range = wave, channels 2*lane, +1).
+template <int NW>
+__device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok) {
+    constexpr int TPT = C / NW;
+    constexpr int SPB = NW / 4;      // token ranges per 16-token block
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = wave * TPT;
+    const int blk = t0 >> 4;
+    const int d0 = 2 * lane;
+
+    f32x2 tau[4];                    // per-block log-decay totals, both channels
+    f32x2 off = {0.f, 0.f};          // log-decay from the block start to this range
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tau[m] = f32x2{0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+        const float2 v = *reinterpret_cast<const float2*>(&sm.Tot[s * DK + d0]);
+        const f32x2 vv = {v.x, v.y};
+        tau[s / SPB] += vv;
+        if (s / SPB == blk && s < wave) off += vv;
+    }
+    // decay from the start of this block to the chunk end (K_restore factor)
+    f32x2 tail = {0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) if (m >= blk) tail += tau[m];
+    const f32x2 eR = {exp_e(tail[0]), exp_e(tail[1])};
+    // decay from the chunk start to the start of this block (K_decay factor)
+    f32x2 head = {0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) if (m < blk) head += tau[m];
+    const f32x2 eP = {exp_e(head[0]), exp_e(head[1])};
+
+    // chunk-level factors, spread over the first four token ranges
+    if (wave == 0) {
+        f32x2 acc = {0.f, 0.f};
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            *reinterpret_cast<float2*>(&sm.P[I * DK + d0]) = make_float2(exp_e(acc[0]), exp_e(acc[1]));
+            acc += tau[I];
+        }
+    } else if (wave == 1 || wave == 2) {
+        // G for pairs (1,0),(2,0),(2,1) on range 1 and (3,0),(3,1),(3,2) on range 2
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+            const int I = (wave == 1) ? (e == 0 ? 1 : 2) : 3;
+            const int J = (wave == 1) ? (e == 2 ? 1 : 0) : e;
+            f32x2 sum = {0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) if (m >= J && m < I) sum += tau[m];
+            const int pidx = I * (I - 1) / 2 + J;
+            *reinterpret_cast<float2*>(&sm.G[pidx * DK + d0]) = make_float2(exp_e(sum[0]), exp_e(sum[1]));
+        }
+    } else if (wave == 3) {
+        const f32x2 all = tau[0] + tau[1] + tau[2] + tau[3];
+        *reinterpret_cast<float2*>(&sm.alast[d0]) = make_float2(exp_e(all[0]), exp_e(all[1]));
+    }
+
+    f32x2 run = off;
+    float kr0[TPT], kr1[TPT], rk0[TPT], rk1[TPT];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+        const int t = t0 + j;
+        const bool ok = t < ntok;
+        run += ok ? in.la[j] : f32x2{0.f, 0.f};
+        const f32x2 bt = {exp_e(run[0]), exp_e(run[1])};     // <= 1
+        const f32x2 ib = {exp_e(-run[0]), exp_e(-run[1])};   // <= exp(80) in range
+        const f32x2 kk = ok ? unpack2(in.k[j]) : f32x2{0.f, 0.f};
+        const f32x2 qq = ok ? unpack2(in.q[j]) : f32x2{0.f, 0.f};
+        const f32x2 kd = kk * bt;
+        const f32x2 ki = kk * ib;
+        *reinterpret_cast<uint32_t*>(&sm.Kd[t * KS + d0]) = pack2(kd[0], kd[1]);
+        *reinterpret_cast<uint32_t*>(&sm.Qd[t * KS + d0]) = pack2(qq[0] * bt[0], qq[1] * bt[1]);
+        *reinterpret_cast<uint32_t*>(&sm.Ki[t * KS + d0]) = pack2(ki[0], ki[1]);
+        kr0[j] = ki[0] * eR[0];                              // decay t+1 .. chunk end
+        kr1[j] = ki[1] * eR[1];
+        const float bta = sm.beta[t];
+        rk0[j] = bta * kd[0] * eP[0];                        // beta_t k_t decay(start .. t)
+        rk1[j] = bta * kd[1] * eP[1];
+    }
+    auto put8 = [&](bf16* dst, const float* x) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]),
+                                                    pack2(x[4], x[5]), pack2(x[6], x[7]));
+    };
+#pragma unroll
+    for (int p = 0; p < TPT / 8; ++p) {
+        put8(&sm.KrT[d0 * TS + t0 + 8 * p], kr0 + 8 * p);
+        put8(&sm.KrT[(d0 + 1) * TS + t0 + 8 * p], kr1 + 8 * p);
+        put8(&sm.RkT[d0 * TS + t0 + 8 * p], rk0 + 8 * p);
+        put8(&sm.RkT[(d0 + 1) * TS + t0 + 8 * p], rk1 + 8 * p);
+    }
+}
+
+// Stage 2: Gram blocks -> -L, M_qk; the wave owning a diagonal block also
+// inverts (I + L_II) in fp32 right away.
+template <int NW>
+__device__ __forceinline__ void stage2(Prep& sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    // Work list per wave, 4 bits per pair index (15 = none), at most 3 pairs.
+    // 8 waves: the diagonal blocks on waves 0-3 (each followed by its
+    // inverse), off-diagonal pairs 2+2+1+1 on waves 4-7. 4 waves: each takes a
+    // diagonal block plus off-diagonal pairs 2, 2, 1, 1.
+    // Pair indices: 0 (0,0) 1 (1,0) 2 (1,1) 3 (2,0) 4 (2,1) 5 (2,2) 6 (3,0) 7 (3,1) 8 (3,2) 9 (3,3).
+    constexpr uint32_t kList8[8] = {0xFF0u, 0xFF2u, 0xFF5u, 0xFF9u, 0xF31u, 0xF64u, 0xFF7u, 0xFF8u};
+    constexpr uint32_t kList4[4] = {0x310u, 0x642u, 0xF75u, 0xF89u};
+    const uint32_t list = (NW == 8) ? kList8[wave] : kList4[wave];
+#pragma unroll
+    for (int slot = 0; slot < 3; ++slot) {
+        const int p = (list >> (4 * slot)) & 15;
+        if (p == 15) break;
+        const int I = (kPairI >> (2 * p)) & 3, J = (kPairJ >> (2 * p)) & 3;
+        const bool diag = I == J;
+        const bf16* rp = sm.Ki + (16 * J + r) * KS + 8 * g;
+        bf16x8 Bk[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) Bk[kk] = ld8(rp + 32 * kk);
+        if (!diag) {
+            const float* gp = sm.G + (I * (I - 1) / 2 + J) * DK + 8 * g;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                Bk[kk] = scale8(Bk[kk], *reinterpret_cast<const f32x4*>(gp + 32 * kk),
+                                *reinterpret_cast<const f32x4*>(gp + 32 * kk + 4));
+        }
+        const bf16* kp = sm.Kd + (16 * I + r) * KS + 8 * g;
+        const bf16* qp = sm.Qd + (16 * I + r) * KS + 8 * g;
+        f32x4 aK = zero4(), aQ = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            aK = mma32(ld8(kp + 32 * kk), Bk[kk], aK);
+            aQ = mma32(ld8(qp + 32 * kk), Bk[kk], aQ);
+        }
+        const int s = 16 * J + r;
+        f32x4 lv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tl = 4 * g + i;              // row inside block I
+            const int t = 16 * I + tl;
+            lv[i] = (!diag || r < tl) ? sm.beta[t] * aK[i] : 0.f;
+            const float mv = (!diag || r <= tl) ? aQ[i] : 0.f;
+            sm.nL[t * TS + s] = (bf16)(-lv[i]);
+            sm.M[t * TS + s] = (bf16)mv;
+        }
+        if (diag) {
+            float* Lt = sm.LdT + I * LDT;
+            *reinterpret_cast<f32x4*>(&Lt[r * 16 + 4 * g]) = lv;
+            lds_fence_wave();
+            // column r of (I + L_II)^{-1}, right-looking substitution
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i == r) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 15; ++m) {
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) x[i] -= Lt[m * 16 + i] * x[m];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if ((i >> 2) == g) sm.D[I * 256 + i * 16 + r] = (bf16)x[i];
+        }
+    }
+}
+
+// Stage 3: Q_decay in place; forward substitution for -W (into Ki) and U0.
+// Tiles: W channel tiles wave, wave + NW (< 8), then the U0 tile at u0col.
+template <int NW, int DVB>
+__device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x4 (&U0)[4]) {
+    constexpr int VS = DVB + 8;
+    constexpr int NWT = 8 / NW;
+    constexpr int NTILE = NWT + 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+
+    for (int idx = tid; idx < C * 64; idx += NW * 64) {
+        const int t = idx >> 6, d = 2 * (idx & 63);
+        uint32_t* p = reinterpret_cast<uint32_t*>(&sm.Qd[t * KS + d]);
+        const f32x2 a = unpack2(*p);
+        const float2 f = *reinterpret_cast<const float2*>(&sm.P[(t >> 4) * DK + d]);
+        *p = pack2(a[0] * f.x, a[1] * f.y);
+    }
+
+    f32x4 X[NTILE][4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 Y[NTILE];
+#pragma unroll
+        for (int tl = 0; tl < NTILE; ++tl) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * I + 4 * g + i;
+                if (tl == NWT) Y[tl][i] = sm.beta[t] * (float)sV[t * VS + u0col + r];
+            }
+            if (tl < NWT) {
+                const int d = 16 * (wave + tl * NW) + r;
+                const bf16x4 rk = *reinterpret_cast<const bf16x4*>(&sm.RkT[d * TS + 16 * I + 4 * g]);
+                Y[tl] = __builtin_convertvector(rk, f32x4);
+            }
+        }
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+            const s16x4 a = ld4(sm.nL + (16 * I + r) * TS + 16 * J + 4 * g);
+#pragma unroll
+            for (int tl = 0; tl < NTILE; ++tl) Y[tl] = mma16(a, pack4(X[tl][J]), Y[tl]);
+        }
+        const s16x4 dI = ld4(sm.D + I * 256 + r * 16 + 4 * g);
+#pragma unroll
+        for (int tl = 0; tl < NTILE; ++tl) X[tl][I] = mma16(dI, pack4(Y[tl]), zero4());
+    }
+#pragma unroll
+    for (int tl = 0; tl < NWT; ++tl) {
+        const int d = 16 * (wave + tl * NW) + r;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.Ki[(16 * I + 4 * g + i) * KS + d] = (bf16)(-X[tl][I][i]);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) U0[I] = X[NWT][I];
+}
+
+// The three state passes for one chunk and this wave's 16 value columns:
+// U = U0 - W S, O = Q_decay S + M_qk U, S = Diag(a_last) S + K_restore^T U.
+// O[I] receives rows 16I + 4g + (0..3) of column r (MFMA accumulator layout).
+// PRELOAD reads all LDS operands of a pass before its MFMAs so the reads
+// overlap (needs ~130 more registers); otherwise each operand is read where
+// it is used.
+template <bool PRELOAD>
+__device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4],
+                                           const bf16* nW, const bf16* Qdec, const bf16* M,
+                                           const bf16* KrT, const float* alast, f32x4 (&O)[4])
+{
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, r = lane & 15;
+    bf16x8 SB[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) SB[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
+
+    f32x4 accU[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        accU[I] = U0[I];
+        O[I] = zero4();
+    }
+    if (PRELOAD) {
+        bf16x8 aW[4][4], aQ[4][4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                aW[I][kk] = ldA_perm(nW + (16 * I + r) * KS, 32 * kk, g);
+                aQ[I][kk] = ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g);
+            }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                accU[I] = mma32(aW[I][kk], SB[kk], accU[I]);
+                O[I] = mma32(aQ[I][kk], SB[kk], O[I]);
+            }
+    } else {
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                accU[I] = mma32(ldA_perm(nW + (16 * I + r) * KS, 32 * kk, g), SB[kk], accU[I]);
+                O[I] = mma32(ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g), SB[kk], O[I]);
+            }
+    }
+    bf16x8 UB[2];
+    UB[0] = pack8(accU[0], accU[1]);
+    UB[1] = pack8(accU[2], accU[3]);
+
+#pragma unroll
+    for (int I = 0; I < 4; ++I) O[I] = mma32(ldA_perm(M + (16 * I + r) * TS, 0, g), UB[0], O[I]);
+    O[2] = mma32(ldA_perm(M + (16 * 2 + r) * TS, 32, g), UB[1], O[2]);
+    O[3] = mma32(ldA_perm(M + (16 * 3 + r) * TS, 32, g), UB[1], O[3]);
+    if (PRELOAD) {
+        bf16x8 aK[8][2];
+        f32x4 al[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            aK[m][0] = ldA_perm(KrT + (16 * m + r) * TS, 0, g);
+            aK[m][1] = ldA_perm(KrT + (16 * m + r) * TS, 32, g);
+            al[m] = *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            Sacc[m] *= al[m];
+            Sacc[m] = mma32(aK[m][0], UB[0], Sacc[m]);
+            Sacc[m] = mma32(aK[m][1], UB[1], Sacc[m]);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            Sacc[m] *= *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
+            Sacc[m] = mma32(ldA_perm(KrT + (16 * m + r) * TS, 0, g), UB[0], Sacc[m]);
+            Sacc[m] = mma32(ldA_perm(KrT + (16 * m + r) * TS, 32, g), UB[1], Sacc[m]);
+        }
+    }
+}
+
+// Store a 64 x 16 output tile (accumulator layout) as bf16, tokens < ntok.
+__device__ __forceinline__ void store_o(const f32x4 (&O)[4], bf16* __restrict__ o, size_t row0,
+                                        size_t rstride, int ncol, int ntok) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * I + 4 * g + i;
+            if (t < ntok) o[(row0 + (size_t)t * rstride) * 128 + ncol] = (bf16)O[I][i];
+        }
+}
 
 }  // namespace mf
 
-template <int DVB>
-__global__ __launch_bounds__(DVB / 16 * 64) void prefill_mfma_kernel(
+// ---------------------------------------------------------------------------
+// Fused kernel: one workgroup per (batch*head, value block of 16*NW columns).
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const float* S0, bf16* __restrict__ o, float* S_final, int T, int H, int NVB)
 {
     using namespace mf;
-    constexpr int NW = DVB / 16;
-    constexpr int NT = NW * 64;
-    constexpr int VS = Smem<DVB>::VS;
-    constexpr int VPR = DVB / 8;                 // 16-byte pieces per value row
-    static_assert((C * VPR) % NT == 0, "value pieces per thread");
-    constexpr int VPT = C * VPR / NT;            // value pieces per thread
+    constexpr int DVB = NW * 16;
+    __shared__ Prep sm;
+    __shared__ bf16 sV[C * (DVB + 8)];
 
-    __shared__ Smem<DVB> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int vb = blockIdx.x % NVB;
+    const int bh = blockIdx.x / NVB;
+    const int b = bh / H, h = bh - b * H;
+    const int col0 = vb * DVB;
+    const int ncol = col0 + 16 * wave + r;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int g = lane >> 4;
-    const int r = lane & 15;
+    for (int i = tid; i < C * TS; i += NW * 64) { sm.nL[i] = (bf16)0.f; sm.M[i] = (bf16)0.f; }
 
-    const int bid = blockIdx.x;
-    const int vb = bid % NVB;
-    const int bh = bid / NVB;
-    const int b = bh / H;
-    const int h = bh - b * H;
-    const int col0 = vb * DVB;                   // first value column of this workgroup
-    const int ncol = col0 + 16 * wave + r;       // this lane's value column in P4
-
-    auto tokrow = [&](int tok) -> size_t { return ((size_t)b * T + tok) * H + h; };
-
-    // zero the triangular buffers once: their upper blocks are never written
-    for (int i = tid; i < C * TS; i += NT) {
-        sm.nL[i] = (bf16)0.f;
-        sm.M[i] = (bf16)0.f;
-    }
-
-    // state tiles: Sacc[m] holds S[16m + 4g + i][ncol]
     f32x4 Sacc[8];
     const size_t sbase = (size_t)bh * DK * 128;
+    if (S0) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            Sacc[m][i] = S0 ? S0[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol] : 0.f;
+            for (int i = 0; i < 4; ++i) Sacc[m][i] = S0[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) Sacc[m] = zero4();
+    }
 
-    // ---- register prefetch of one chunk's inputs
-    const bool p1 = tid < 256;              // threads doing the elementwise chunk prep
-    const int dp = tid & 63;                // channel pair 2dp, 2dp+1
-    const int blk = (tid >> 6) & 3;         // 16-token block
-    uint32_t pk[16], pq[16];
-    float pla0[16], pla1[16];
-    uint4 pv[VPT];
-    float pb = 0.f;
-
-    auto prefetch = [&](int c) {
-        if (p1) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int tok = c * C + blk * 16 + j;
-                if (tok < T) {
-                    const size_t base = tokrow(tok) * DK + 2 * dp;
-                    pk[j] = *reinterpret_cast<const uint32_t*>(k + base);
-                    pq[j] = *reinterpret_cast<const uint32_t*>(q + base);
-                    const float2 l2 = *reinterpret_cast<const float2*>(log_alpha + base);
-                    pla0[j] = l2.x;
-                    pla1[j] = l2.y;
-                } else {
-                    pk[j] = 0u; pq[j] = 0u; pla0[j] = 0.f; pla1[j] = 0.f;
-                }
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < VPT; ++p) {
-            const int piece = tid + p * NT;
-            const int t = piece / VPR, c8 = piece - t * VPR;
-            const int tok = c * C + t;
-            pv[p] = tok < T ? *reinterpret_cast<const uint4*>(v + tokrow(tok) * 128 + col0 + 8 * c8)
-                            : make_uint4(0u, 0u, 0u, 0u);
-        }
-        if (tid < C) {
-            const int tok = c * C + tid;
-            pb = tok < T ? beta[tokrow(tok)] : 0.f;
-        }
-    };
-
+    Inputs<NW> in;
     const int nchunks = (T + C - 1) / C;
-    if (nchunks > 0) prefetch(0);
+    if (nchunks > 0) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, 0, col0);
 
     for (int c = 0; c < nchunks; ++c) {
-        __syncthreads();  // previous chunk's readers are done with every buffer
-
-        // ---- P1a: block sums of the log-decay; values and beta to LDS
-        if (p1) {
-            float run0 = 0.f, run1 = 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) { run0 += pla0[j]; run1 += pla1[j]; }
-            sm.Tot[blk * DK + 2 * dp] = run0;
-            sm.Tot[blk * DK + 2 * dp + 1] = run1;
-        }
-#pragma unroll
-        for (int p = 0; p < VPT; ++p) {
-            const int piece = tid + p * NT;
-            const int t = piece / VPR, c8 = piece - t * VPR;
-            *reinterpret_cast<uint4*>(&sm.V[t * VS + 8 * c8]) = pv[p];
-        }
-        if (tid < C) sm.beta[tid] = pb;
-        __syncthreads();
-
-        // ---- P1b: decay-scaled operands (block-local cumulative log-decay c_t)
-        if (p1) {
-            float tot[2][4];
-#pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                tot[0][J] = sm.Tot[J * DK + 2 * dp];
-                tot[1][J] = sm.Tot[J * DK + 2 * dp + 1];
-            }
-            float fP[2], fT[2], fR[2], g1[2], g2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float logP = 0.f, total = 0.f, myT = 0.f;
-#pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    if (J < blk) logP += tot[e][J];
-                    if (J == blk) myT = tot[e][J];
-                    total += tot[e][J];
-                }
-                const int d = 2 * dp + e;
-                fP[e] = exp_e(logP);
-                if (blk == 3) sm.alast[d] = exp_e(total);
-                sm.P[blk * DK + d] = fP[e];
-                fT[e] = exp_e(myT);                    // decay over the whole block
-                fR[e] = exp_e(total - logP - myT);     // block end -> chunk end
-                g1[e] = blk == 0 ? exp_e(tot[e][1]) : (blk == 1 ? exp_e(tot[e][2]) : 0.f);
-                g2[e] = blk == 0 ? exp_e(tot[e][1] + tot[e][2]) : 0.f;
-            }
-            float run0 = 0.f, run1 = 0.f;
-            uint32_t kr0[8], kr1[8];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                run0 += pla0[j];
-                run1 += pla1[j];
-                const float b0 = exp_e(run0), b1 = exp_e(run1);      // <= 1
-                const float i0 = exp_e(-run0), i1 = exp_e(-run1);    // <= exp(80) in range
-                const float k0 = lo_bf(pk[j]), k1 = hi_bf(pk[j]);
-                const float q0 = lo_bf(pq[j]), q1 = hi_bf(pq[j]);
-                const int t = blk * 16 + j;
-                const float ki0 = k0 * i0, ki1 = k1 * i1;
-                const float ke0 = ki0 * fT[0], ke1 = ki1 * fT[1];    // decay t+1 .. block end
-                *reinterpret_cast<uint32_t*>(&sm.Kd[t * KS + 2 * dp]) = pack2(k0 * b0, k1 * b1);
-                *reinterpret_cast<uint32_t*>(&sm.Qd[t * KS + 2 * dp]) = pack2(q0 * b0, q1 * b1);
-                *reinterpret_cast<uint32_t*>(&sm.Ki[t * KS + 2 * dp]) = pack2(ki0, ki1);
-                if (blk < 3)
-                    *reinterpret_cast<uint32_t*>(&sm.Ke[t * KS + 2 * dp]) = pack2(ke0, ke1);
-                if (blk == 0) {
-                    *reinterpret_cast<uint32_t*>(&sm.Ke[(48 + j) * KS + 2 * dp]) =
-                        pack2(ke0 * g1[0], ke1 * g1[1]);   // pair (2,0)
-                    *reinterpret_cast<uint32_t*>(&sm.Ke[(64 + j) * KS + 2 * dp]) =
-                        pack2(ke0 * g2[0], ke1 * g2[1]);   // pair (3,0)
-                }
-                if (blk == 1)
-                    *reinterpret_cast<uint32_t*>(&sm.Ke[(80 + j) * KS + 2 * dp]) =
-                        pack2(ke0 * g1[0], ke1 * g1[1]);   // pair (3,1)
-                // K_restore: decay t+1 .. chunk end, two tokens per 32-bit word
-                const float r0 = ke0 * fR[0], r1 = ke1 * fR[1];
-                if (j & 1) {
-                    kr0[j >> 1] |= (uint32_t)bf16_bits(r0) << 16;
-                    kr1[j >> 1] |= (uint32_t)bf16_bits(r1) << 16;
-                } else {
-                    kr0[j >> 1] = bf16_bits(r0);
-                    kr1[j >> 1] = bf16_bits(r1);
-                }
-            }
-            uint4* d0 = reinterpret_cast<uint4*>(&sm.KrT[(2 * dp) * TS + blk * 16]);
-            uint4* d1 = reinterpret_cast<uint4*>(&sm.KrT[(2 * dp + 1) * TS + blk * 16]);
-            d0[0] = make_uint4(kr0[0], kr0[1], kr0[2], kr0[3]);
-            d0[1] = make_uint4(kr0[4], kr0[5], kr0[6], kr0[7]);
-            d1[0] = make_uint4(kr1[0], kr1[1], kr1[2], kr1[3]);
-            d1[1] = make_uint4(kr1[4], kr1[5], kr1[6], kr1[7]);
-        }
-        // the registers are free again: start loading the next chunk
-        if (c + 1 < nchunks) prefetch(c + 1);
-        __syncthreads();
-
-        // ---- P2: intra-chunk Gram blocks -> -L (bf16), L diag blocks (fp32), M_qk
-        for (int p = wave; p < 20; p += NW) {
-            const int pi = p % 10;
-            const bool isK = p < 10;
-            const int I = kPairI[pi], J = kPairJ[pi];
-            const bf16* left = (isK ? sm.Kd : sm.Qd) + (16 * I + r) * KS;
-            const bf16* right;
-            if (J == I) right = sm.Ki + (16 * I + r) * KS;
-            else if (J == I - 1) right = sm.Ke + (16 * J + r) * KS;
-            else right = sm.Ke + ((I == 2 ? 48 : (J == 0 ? 64 : 80)) + r) * KS;
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc = mma32(ld8(left + 32 * kk + 8 * g), ld8(right + 32 * kk + 8 * g), acc);
-            const int s = 16 * J + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * I + 4 * g + i;
-                if (isK) {
-                    const float val = (J < I || s < t) ? sm.beta[t] * acc[i] : 0.f;
-                    sm.nL[t * TS + s] = (bf16)(-val);
-                    if (J == I) sm.Ld[I * LDS_ + (4 * g + i) * 16 + r] = val;
-                } else {
-                    sm.M[t * TS + s] = (bf16)((J < I || s <= t) ? acc[i] : 0.f);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- P2b: inverses of the diagonal blocks (wave 0), Q_decay (everyone)
-        if (wave == 0) {
-            // lane (g, r): column r of (I + L_gg)^{-1} by forward substitution
-            const float* Lb = sm.Ld + g * LDS_;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == r) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc -= Lb[i * 16 + m] * x[m];
-                x[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm.D[g * 256 + i * 16 + r] = (bf16)x[i];
-        }
-        bf16* Qdec = sm.Ke;  // Gram right operands are dead now
-        for (int idx = tid; idx < C * 64; idx += NT) {
-            const int t = idx >> 6, d = 2 * (idx & 63);
-            const int I = t >> 4;
-            const uint32_t u = *reinterpret_cast<const uint32_t*>(&sm.Qd[t * KS + d]);
-            const float a0 = mf::lo_bf(u) * sm.P[I * DK + d];
-            const float a1 = mf::hi_bf(u) * sm.P[I * DK + d + 1];
-            *reinterpret_cast<uint32_t*>(&Qdec[t * KS + d]) = mf::pack2(a0, a1);
-        }
-        __syncthreads();
-
-        // ---- P3: W = INV Diag(beta) K_decay (stored negated) and U0 = INV Diag(beta) V
-        bf16* nW = sm.Ki;   // Gram right operands are dead now
+        lds_barrier();
+        stage1a<NW, DVB>(sm, sV, in, T - c * C);
+        lds_barrier();
+        stage1b<NW>(sm, in, T - c * C);
+        if (c + 1 < nchunks) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
+        lds_barrier();
+        stage2<NW>(sm);
+        lds_barrier();
         f32x4 U0[4];
-        constexpr int NWT = 8 / NW;   // W channel tiles per wave
-        static_assert(NWT * NW == 8, "waves must divide the 8 key-channel tiles");
-#pragma unroll
-        for (int rep = 0; rep <= NWT; ++rep) {
-            // tiles: W channel tiles wave, wave+NW (< 8), then this wave's U0 tile
-            const bool isU = rep == NWT;
-            const int ct = wave + rep * NW;
-            f32x4 X[4];
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 Y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * I + 4 * g + i;
-                    Y[i] = isU ? sm.beta[t] * (float)sm.V[t * VS + 16 * wave + r]
-                               : sm.beta[t] * (float)sm.Kd[t * KS + 16 * ct + r] *
-                                     sm.P[I * DK + 16 * ct + r];
-                }
-#pragma unroll
-                for (int J = 0; J < I; ++J)
-                    Y = mma16(ld4(sm.nL + (16 * I + r) * TS + 16 * J + 4 * g), pack4(X[J]), Y);
-                X[I] = mma16(ld4(sm.D + I * 256 + r * 16 + 4 * g), pack4(Y), zero4());
-            }
-            if (isU) {
-#pragma unroll
-                for (int I = 0; I < 4; ++I) U0[I] = X[I];
-            } else {
-#pragma unroll
-                for (int I = 0; I < 4; ++I)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        nW[(16 * I + 4 * g + i) * KS + 16 * ct + r] = (bf16)(-X[I][i]);
-            }
-        }
-        __syncthreads();
-
-        // ---- P4: state-dependent chain for this wave's 16 value columns
-        bf16x8 SB[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) SB[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
-
-        f32x4 accU[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            accU[I] = U0[I];
-            const bf16* rowp = nW + (16 * I + r) * KS;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) accU[I] = mma32(mf::ldA_perm(rowp, 32 * kk, g), SB[kk], accU[I]);
-        }
-        bf16x8 UB[2];
-        UB[0] = pack8(accU[0], accU[1]);
-        UB[1] = pack8(accU[2], accU[3]);
-
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            f32x4 acc = zero4();
-            const bf16* qrow = Qdec + (16 * I + r) * KS;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mma32(mf::ldA_perm(qrow, 32 * kk, g), SB[kk], acc);
-            const bf16* mrow = sm.M + (16 * I + r) * TS;
-            acc = mma32(mf::ldA_perm(mrow, 0, g), UB[0], acc);
-            if (I >= 2) acc = mma32(mf::ldA_perm(mrow, 32, g), UB[1], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = c * C + 16 * I + 4 * g + i;
-                if (tok < T) o[tokrow(tok) * 128 + ncol] = (bf16)acc[i];
-            }
-        }
-
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Sacc[m][i] *= sm.alast[16 * m + 4 * g + i];
-            const bf16* krow = sm.KrT + (16 * m + r) * TS;
-            Sacc[m] = mma32(mf::ldA_perm(krow, 0, g), UB[0], Sacc[m]);
-            Sacc[m] = mma32(mf::ldA_perm(krow, 32, g), UB[1], Sacc[m]);
-        }
+        stage3<NW, DVB>(sm, sV, 16 * wave, U0);
+        lds_barrier();
+        f32x4 O[4];
+        state_pass<(NW < 8)>(Sacc, U0, sm.Ki, sm.Qd, sm.M, sm.KrT, sm.alast, O);
+        store_o(O, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, ncol, T - c * C);
     }
 
     if (S_final) {
@@ -413,26 +561,205 @@ __global__ __launch_bounds__(DVB / 16 * 64) void prefill_mfma_kernel(
     }
 }
 
+// Prep kernel: chunks [c0, c0 + cpw) of one head; writes operand records.
+__global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    char* __restrict__ ws, int T, int H, int cpw)
+{
+    using namespace mf;
+    constexpr int NW = 8, DVB = 128;
+    __shared__ Prep sm;
+    __shared__ bf16 sV[C * (DVB + 8)];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nchunks = (T + C - 1) / C;
+    const int ngrp = (nchunks + cpw - 1) / cpw;
+    const int bh = blockIdx.x / ngrp;
+    const int c0 = (blockIdx.x - bh * ngrp) * cpw;
+    const int c1 = min(c0 + cpw, nchunks);
+    const int b = bh / H, h = bh - b * H;
+
+    for (int i = tid; i < C * TS; i += NW * 64) { sm.nL[i] = (bf16)0.f; sm.M[i] = (bf16)0.f; }
+
+    Inputs<NW> in;
+    if (c0 < c1) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c0, 0);
+    for (int c = c0; c < c1; ++c) {
+        lds_barrier();
+        stage1a<NW, DVB>(sm, sV, in, T - c * C);
+        lds_barrier();
+        stage1b<NW>(sm, in, T - c * C);
+        if (c + 1 < c1) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
+        lds_barrier();
+        stage2<NW>(sm);
+        lds_barrier();
+        f32x4 U0[4];
+        stage3<NW, DVB>(sm, sV, 16 * wave, U0);
+        lds_barrier();
+        char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES;
+        // LDS-staged regions, copied verbatim
+        auto copy = [&](int off, const void* src, int bytes) {
+            const uint4* s = reinterpret_cast<const uint4*>(src);
+            uint4* d = reinterpret_cast<uint4*>(rec + off);
+            for (int i = tid; i < bytes / 16; i += NW * 64) d[i] = s[i];
+        };
+        copy(REC_NW, sm.Ki, C * KS * 2);
+        copy(REC_QD, sm.Qd, C * KS * 2);
+        copy(REC_KR, sm.KrT, DK * TS * 2);
+        copy(REC_M, sm.M, C * TS * 2);
+        copy(REC_AL, sm.alast, DK * 4);
+        // U0 tile (I, wave) in accumulator order: 4 bf16 per lane
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            uint2 u;
+            u.x = pack2(U0[I][0], U0[I][1]);
+            u.y = pack2(U0[I][2], U0[I][3]);
+            *reinterpret_cast<uint2*>(rec + REC_U0 + ((I * 8 + wave) * 64 + lane) * 8) = u;
+        }
+    }
+}
+
+// State kernel: one wave per (batch*head, 16 value columns). It has no
+// barriers: each chunk's operand record is copied into LDS with direct
+// global-to-LDS loads one chunk ahead (double buffer), and the loads are
+// waited for explicitly. The 8 column tiles of a head are placed on the same
+// XCD (block ids that share id % 8), so they share that XCD's L2 copy of the
+// records.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr), "v"(gptr) : "memory");
+}
+
+__global__ __launch_bounds__(64, 1) void prefill_state_kernel(
+    const char* __restrict__ ws, const float* S0, bf16* __restrict__ o, float* S_final,
+    int T, int H, int BH)
+{
+    using namespace mf;
+    __shared__ __attribute__((aligned(16))) char buf[2][REC_LDS];
+
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, r = lane & 15;
+    const int grp = blockIdx.x >> 6;
+    const int bh = grp * 8 + (blockIdx.x & 7);
+    const int ct = (blockIdx.x >> 3) & 7;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh - b * H;
+    const int ncol = 16 * ct + r;
+    const int nchunks = (T + C - 1) / C;
+
+    f32x4 Sacc[8];
+    const size_t sbase = (size_t)bh * DK * 128;
+    if (S0) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sacc[m][i] = S0[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) Sacc[m] = zero4();
+    }
+
+    constexpr int FULL = REC_LDS / 1024;          // whole 1 KB pieces
+    constexpr int REST = (REC_LDS % 1024) / 16;   // lanes of the partial piece
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)buf[0]);
+    auto stage = [&](int c) {
+        const char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES + lane * 16;
+        const uint32_t dst = lds0 + (uint32_t)((c & 1) * REC_LDS);
+#pragma unroll 4
+        for (int p = 0; p < FULL; ++p) lds_dma16(dst + p * 1024, rec + p * 1024);
+        if (REST > 0 && lane < REST) lds_dma16(dst + FULL * 1024, rec + FULL * 1024);
+    };
+    auto load_u0 = [&](int c, uint2 (&u)[4]) {
+        const char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES + REC_U0;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+            u[I] = *reinterpret_cast<const uint2*>(rec + ((I * 8 + ct) * 64 + lane) * 8);
+    };
+
+    uint2 u0raw[4];
+    f32x4 Oprev[4];
+    if (nchunks > 0) {
+        stage(0);
+        load_u0(0, u0raw);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        // Everything issued so far has landed: this chunk's record and U0,
+        // and the previous chunk's output stores.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        f32x4 U0[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x2 lo = unpack2(u0raw[I].x), hi = unpack2(u0raw[I].y);
+            U0[I] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        if (c + 1 < nchunks) {
+            stage(c + 1);
+            load_u0(c + 1, u0raw);
+        }
+        // the previous chunk's outputs leave now, behind this chunk's loads
+        if (c > 0) store_o(Oprev, o, ((size_t)b * T + (size_t)(c - 1) * C) * H + h, (size_t)H, ncol, C);
+        const char* sb = buf[c & 1];
+        state_pass<true>(Sacc, U0, reinterpret_cast<const bf16*>(sb + REC_NW),
+                   reinterpret_cast<const bf16*>(sb + REC_QD), reinterpret_cast<const bf16*>(sb + REC_M),
+                   reinterpret_cast<const bf16*>(sb + REC_KR), reinterpret_cast<const float*>(sb + REC_AL),
+                   Oprev);
+        // LDS reads of buf[c & 1] must finish before chunk c + 2 refills it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    if (nchunks > 0)
+        store_o(Oprev, o, ((size_t)b * T + (size_t)(nchunks - 1) * C) * H + h, (size_t)H, ncol,
+                T - (nchunks - 1) * C);
+
+    if (S_final) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S_final[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+constexpr long kSplitBelowHeads = 128;   // fewer heads than this: prep + state kernels
+}
+
 bool prefill_mfma_supported(int dk, int dv, int chunk) {
     return dk == 128 && dv == 128 && (chunk == 64 || chunk == 0);
 }
 
+size_t prefill_mfma_workspace(int B, int T, int H) {
+    const long heads = (long)B * H;
+    if (heads >= kSplitBelowHeads || T <= 0) return 0;
+    const size_t nchunks = ((size_t)T + mf::C - 1) / mf::C;
+    return (size_t)heads * nchunks * mf::REC_BYTES;
+}
+
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
                                const float* beta, const float* S0, void* o, float* S_final,
-                               int B, int T, int H, hipStream_t st)
+                               int B, int T, int H, void* ws, hipStream_t st)
 {
     const long heads = (long)B * H;
-    // One workgroup per head when that fills the chip; otherwise split the
-    // value columns in two to double the workgroup count.
-    if (heads >= 256) {
-        hipLaunchKernelGGL(prefill_mfma_kernel<128>, dim3((unsigned)heads), dim3(512), 0, st,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
-                           (bf16*)o, S_final, T, H, 1);
-    } else {
-        hipLaunchKernelGGL(prefill_mfma_kernel<64>, dim3((unsigned)(heads * 2)), dim3(256), 0, st,
+    if (heads >= kSplitBelowHeads) {
+        hipLaunchKernelGGL(prefill_fused_kernel<4>, dim3((unsigned)(heads * 2)), dim3(256), 0, st,
                            (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
                            (bf16*)o, S_final, T, H, 2);
+        return hipGetLastError();
     }
+    // few heads: chunk-parallel prep, then the state walk
+    const long nchunks = (T + mf::C - 1) / mf::C;
+    const long work = heads * nchunks;
+    int cpw = (int)((work + 255) / 256);          // about one workgroup per CU
+    if (cpw < 1) cpw = 1;
+    const long ngrp = (nchunks + cpw - 1) / cpw;
+    hipLaunchKernelGGL(prefill_prep_kernel, dim3((unsigned)(heads * ngrp)), dim3(512), 0, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, (char*)ws, T, H,
+                       cpw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long groups = (heads + 7) / 8;   // 8 heads x 8 column tiles per group of 64 blocks
+    hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)(groups * 64)), dim3(64), 0, st,
+                       (const char*)ws, S0, (bf16*)o, S_final, T, H, (int)heads);
     return hipGetLastError();
 }
 

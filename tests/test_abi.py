@@ -51,7 +51,7 @@ def P(i, off=0):
 
 
 def prefill(lib, *, q=P(0), k=P(1), v=P(2), la=P(3), beta=P(4), S0=P(5), o=P(6), Sf=P(7),
-            B=1, T=64, H=2, dk=128, dv=128, dt=1, chunk=64, ws=None, ws_bytes=0):
+            B=1, T=64, H=2, dk=128, dv=128, dt=1, chunk=64, ws=P(10), ws_bytes=1 << 30):
     return lib.kda_prefill_fwd(q, k, v, la, beta, S0, o, Sf, B, T, H, dk, dv, dt, chunk,
                                ws, ws_bytes, None)
 
@@ -88,7 +88,22 @@ def test_prefill_empty_batch_is_noop(lib):
 
 
 def test_workspace_query(lib):
+    # many heads: fused kernel, no workspace; few heads: chunk-parallel prep
     assert lib.kda_prefill_workspace_size(8, 8192, 32, 128, 128, 1, 64) == 0
+    n = lib.kda_prefill_workspace_size(1, 4096, 16, 128, 128, 1, 64)
+    assert n > 0 and n % 256 == 0
+    assert lib.kda_prefill_workspace_size(1, 4096 + 1, 16, 128, 128, 1, 64) > n  # ragged tail
+    assert lib.kda_prefill_workspace_size(1, 4096, 16, 128, 128, 0, 64) == 0    # fp32 path
+    assert lib.kda_prefill_workspace_size(1, 0, 16, 128, 128, 1, 64) == 0
+
+
+def test_workspace_rejects(lib):
+    need = lib.kda_prefill_workspace_size(1, 64, 2, 128, 128, 1, 64)
+    assert prefill(lib, ws=None, ws_bytes=0) == WORKSPACE
+    assert prefill(lib, ws=P(10), ws_bytes=need - 1) == WORKSPACE
+    assert prefill(lib, ws=P(10, 8), ws_bytes=need) == INVALID     # misaligned
+    assert prefill(lib, ws=P(0, 512), ws_bytes=need) == INVALID    # overlaps q
+    assert prefill(lib, ws=P(6), ws_bytes=need) == INVALID         # overlaps o
 
 
 def test_decode_rejects(lib):

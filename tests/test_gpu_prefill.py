@@ -61,6 +61,41 @@ def test_bf16_mfma_small(T):
     report(f"bf16 B2 H3 T{T} D128 C64 with S0", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
+def test_bf16_fused_half_width_path():
+    # 128..255 heads: the fused kernel with 64-column workgroups
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=2, T=130, H=64)
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report("bf16 B2 H64 T130 (fused, 64-column blocks)", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_bf16_fused_full_width_path(with_s0):
+    # 256+ heads: the fused kernel with one 128-column workgroup per head
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=4, T=130, H=64)
+    if not with_s0:
+        x["S0"] = None
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report(f"bf16 B4 H64 T130 (fused, 128-column blocks, S0={with_s0})",
+           [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+def test_bf16_workspace_given_by_caller():
+    # few heads use the chunk-parallel prep + state kernels through a workspace
+    c = W.PREFILL_CONFIGS["prefill"]
+    x = W.prefill_inputs(c, B=1, T=333, H=5)
+    xd = to_dev(x)
+    n = kda.kda_prefill_workspace_size(1, 333, 5, 128, 128, torch.bfloat16)
+    assert n > 0
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device=DEV)
+    o, S = gpu_prefill(xd, workspace=ws)
+    ro, rS = oracle_prefill(x)
+    report("bf16 B1 H5 T333 with caller workspace", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
 def test_bf16_prefill_config_full():
     c = W.PREFILL_CONFIGS["prefill"]
     x = W.prefill_inputs(c)
@@ -85,10 +120,11 @@ def test_bf16_batched_config_sampled():
 
 def test_bf16_long_config_sampled():
     """1M-token context at full size. Sampled heads are checked on the first
-    65536 tokens exactly, and on the last 65536 tokens from a zero state: the
-    state entering that window is damped by the product over the window of the
-    largest per-step decay, which the test computes and requires to be
-    negligible against the tolerance."""
+    65536 tokens exactly, and at the end against a run of the last 65536
+    tokens from a zero state: the state entering that window is damped by the
+    product of the largest per-step decay over the window, which the test
+    computes and requires to be negligible against the tolerance (outputs are
+    compared only in the second half of the window, where the same holds)."""
     c = W.PREFILL_CONFIGS["long"]
     T, H, D = c.T, c.H, c.dk
     q = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=DEV)
@@ -114,13 +150,21 @@ def test_bf16_long_config_sampled():
                                    head(la, first), head(beta, first), None)
         report(f"long config first {Wn} tokens, head {h}", [("o", o[:, first, h:h + 1], ro)],
                TOL_BF16)
+        # Window from a zero state: the history entering it is damped by the
+        # product of the largest per-step decay over the tokens before the
+        # compared position. Outputs are compared only past `skip` tokens.
         last = slice(T - Wn, T)
-        damp = float(torch.exp(la[0, last, h].double().max(dim=-1).values.sum()))
-        assert damp < 1e-6, damp
+        skip = Wn // 2
+        lmax = la[0, last, h].double().max(dim=-1).values
+        damp_o = float(torch.exp(lmax[:skip].sum()))
+        damp_s = float(torch.exp(lmax.sum()))
+        assert damp_o < 1e-6 and damp_s < 1e-6, (damp_o, damp_s)
         ro, rS = oracle.prefill_f64(head(q, last), head(k, last), head(v, last),
                                     head(la, last), head(beta, last), None)
-        report(f"long config last {Wn} tokens + final state, head {h} (damping {damp:.1e})",
-               [("o", o[:, last, h:h + 1], ro), ("S", S[:, h:h + 1], rS)], TOL_BF16)
+        report(f"long config last {Wn - skip} tokens + final state, head {h} "
+               f"(damping {damp_o:.1e} / {damp_s:.1e})",
+               [("o", o[:, T - Wn + skip:, h:h + 1], ro[:, skip:]), ("S", S[:, h:h + 1], rS)],
+               TOL_BF16)
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])

@@ -33,6 +33,8 @@ def _compile(src: str) -> str:
 
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
+    if os.path.exists(LIB):
+        os.remove(LIB)   # never leave a stale library behind a failed build
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

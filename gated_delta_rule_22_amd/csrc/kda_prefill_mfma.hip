@@ -31,11 +31,11 @@
 //    inputs are loaded into registers while the current one computes.
 //  * prep_kernel + state_kernel: for few heads. The prep kernel runs the
 //    state-independent work of many chunks in parallel and writes, per
-//    chunk-head, -W, Q_decay, K_restore^T, M_qk (bf16, in the padded layout
-//    the state kernel keeps in LDS), U0 and a_last to a workspace. The state
+//    chunk-head, -W, Q_decay, K_restore^T, M_qk (bf16, in MFMA operand
+//    register order), U0 and a_last to a workspace. The state
 //    kernel then walks the chunks in order doing only the three state
-//    passes (one wave per 16 value columns), streaming each chunk's operands
-//    into LDS with direct global-to-LDS loads one chunk ahead.
+//    passes, one wave per 16 value columns, loading each chunk's operands
+//    straight into MFMA registers while the previous chunk computes.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -70,17 +70,25 @@ struct Prep {
     float beta[C];
 };
 
-// Operand record written by the prep kernel, read by the state kernel.
-// Offsets in bytes; the first five regions are copied verbatim into LDS.
+// Operand record written by the prep kernel, read by the state kernel, in
+// MFMA register order: each A operand of a 16x16x32 step is 1 KB, 16 bytes
+// per lane in lane order, so a wave loads it with one coalesced dwordx4
+// load straight into the registers the MFMA reads.
+//   NW  : -W      operands (I, kk), I, kk in 0..3          16 KB
+//   QD  : Q_decay operands (I, kk)                          16 KB
+//   M   : M_qk    operands (0,0),(1,0),(2,0),(3,0),(2,1),(3,1)  6 KB
+//   KR  : K_restore^T operands (m, kk), m in 0..7, kk in 0..1  16 KB
+//   AL  : a_last, 128 fp32
+//   U0  : U0 tiles (I, value tile ct) in accumulator order, bf16   16 KB
+constexpr int OPB = 1024;
 constexpr int REC_NW = 0;
-constexpr int REC_QD = REC_NW + C * KS * 2;
-constexpr int REC_KR = REC_QD + C * KS * 2;
-constexpr int REC_M = REC_KR + DK * TS * 2;
-constexpr int REC_AL = REC_M + C * TS * 2;
-constexpr int REC_LDS = REC_AL + DK * 4;          // bytes staged into LDS per chunk
-constexpr int REC_U0 = REC_LDS;                   // U0, bf16, MFMA accumulator-tile order
+constexpr int REC_QD = REC_NW + 16 * OPB;
+constexpr int REC_M = REC_QD + 16 * OPB;
+constexpr int REC_KR = REC_M + 6 * OPB;
+constexpr int REC_AL = REC_KR + 16 * OPB;
+constexpr int REC_U0 = REC_AL + DK * 4;
 constexpr int REC_BYTES = REC_U0 + C * 128 * 2;
-static_assert(REC_LDS % 16 == 0 && REC_BYTES % 256 == 0, "record alignment");
+static_assert(REC_BYTES % 256 == 0, "record alignment");
 
 // The 10 lower block pairs (I, J), row-major, 2 bits per entry.
 constexpr uint32_t kPairI = (0u << 0) | (1u << 2) | (1u << 4) | (2u << 6) | (2u << 8) |
@@ -405,10 +413,15 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
 // PRELOAD reads all LDS operands of a pass before its MFMAs so the reads
 // overlap (needs ~130 more registers); otherwise each operand is read where
 // it is used.
-template <bool PRELOAD>
+// `between(k)` is called after the k-th of four MFMA groups (k = 0..3) so a
+// caller can slot other instructions (the next chunk's loads) under the MFMAs.
+struct NoOp { __device__ void operator()(int) const {} };
+
+template <bool PRELOAD, typename Between = NoOp>
 __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4],
                                            const bf16* nW, const bf16* Qdec, const bf16* M,
-                                           const bf16* KrT, const float* alast, f32x4 (&O)[4])
+                                           const bf16* KrT, const float* alast, f32x4 (&O)[4],
+                                           Between between = Between())
 {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, r = lane & 15;
@@ -431,13 +444,18 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
                 aW[I][kk] = ldA_perm(nW + (16 * I + r) * KS, 32 * kk, g);
                 aQ[I][kk] = ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g);
             }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 accU[I] = mma32(aW[I][kk], SB[kk], accU[I]);
                 O[I] = mma32(aQ[I][kk], SB[kk], O[I]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            between(kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -464,6 +482,7 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
             aK[m][1] = ldA_perm(KrT + (16 * m + r) * TS, 32, g);
             al[m] = *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             Sacc[m] *= al[m];
@@ -597,17 +616,28 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         stage3<NW, DVB>(sm, sV, 16 * wave, U0);
         lds_barrier();
         char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES;
-        // LDS-staged regions, copied verbatim
-        auto copy = [&](int off, const void* src, int bytes) {
-            const uint4* s = reinterpret_cast<const uint4*>(src);
-            uint4* d = reinterpret_cast<uint4*>(rec + off);
-            for (int i = tid; i < bytes / 16; i += NW * 64) d[i] = s[i];
-        };
-        copy(REC_NW, sm.Ki, C * KS * 2);
-        copy(REC_QD, sm.Qd, C * KS * 2);
-        copy(REC_KR, sm.KrT, DK * TS * 2);
-        copy(REC_M, sm.M, C * TS * 2);
-        copy(REC_AL, sm.alast, DK * 4);
+        const int g = lane >> 4, r = lane & 15;
+        // 54 A operands, spread over the waves: 16 B per lane each
+        for (int j = wave; j < 54; j += NW) {
+            const bf16* rowp;
+            int k0, off;
+            if (j < 16) {              // -W (I = j / 4, kk = j % 4)
+                rowp = sm.Ki + (16 * (j >> 2) + r) * KS; k0 = 32 * (j & 3); off = REC_NW + j * OPB;
+            } else if (j < 32) {       // Q_decay
+                const int jj = j - 16;
+                rowp = sm.Qd + (16 * (jj >> 2) + r) * KS; k0 = 32 * (jj & 3); off = REC_QD + jj * OPB;
+            } else if (j < 38) {       // M_qk
+                const int jj = j - 32;
+                const int I = jj < 4 ? jj : jj - 2, kk = jj < 4 ? 0 : 1;
+                rowp = sm.M + (16 * I + r) * TS; k0 = 32 * kk; off = REC_M + jj * OPB;
+            } else {                   // K_restore^T (m = jj / 2, kk = jj % 2)
+                const int jj = j - 38;
+                rowp = sm.KrT + (16 * (jj >> 1) + r) * TS; k0 = 32 * (jj & 1); off = REC_KR + jj * OPB;
+            }
+            *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = ldA_perm(rowp, k0, g);
+        }
+        if (tid < DK / 4)
+            *reinterpret_cast<f32x4*>(rec + REC_AL + tid * 16) = *reinterpret_cast<const f32x4*>(&sm.alast[4 * tid]);
         // U0 tile (I, wave) in accumulator order: 4 bf16 per lane
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -619,29 +649,22 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     }
 }
 
-// State kernel: one wave per (batch*head, 16 value columns). It has no
-// barriers: each chunk's operand record is copied into LDS with direct
-// global-to-LDS loads one chunk ahead (double buffer), and the loads are
-// waited for explicitly. The 8 column tiles of a head are placed on the same
-// XCD (block ids that share id % 8), so they share that XCD's L2 copy of the
-// records.
-__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds_addr), "v"(gptr) : "memory");
-}
-
+// State kernel: one wave per (batch*head, 16 value columns), no LDS and no
+// barriers. Each chunk's A operands arrive straight into registers from the
+// operand record (L2-resident: the 8 column waves of a head read the same
+// record and sit on the same XCD, block ids sharing id % 8). Every operand
+// set is reloaded for the next chunk right after its last use in this chunk,
+// so its loads overlap the rest of this chunk's MFMAs.
 __global__ __launch_bounds__(64, 1) void prefill_state_kernel(
     const char* __restrict__ ws, const float* S0, bf16* __restrict__ o, float* S_final,
     int T, int H, int BH)
 {
     using namespace mf;
-    __shared__ __attribute__((aligned(16))) char buf[2][REC_LDS];
-
     const int lane = threadIdx.x;
     const int g = lane >> 4, r = lane & 15;
     const int grp = blockIdx.x >> 6;
     const int bh = grp * 8 + (blockIdx.x & 7);
-    const int ct = (blockIdx.x >> 3) & 7;
+    const int ct = (blockIdx.x >> 3) & 7;          // value column tile
     if (bh >= BH) return;
     const int b = bh / H, h = bh - b * H;
     const int ncol = 16 * ct + r;
@@ -658,57 +681,91 @@ __global__ __launch_bounds__(64, 1) void prefill_state_kernel(
 #pragma unroll
         for (int m = 0; m < 8; ++m) Sacc[m] = zero4();
     }
+    if (nchunks == 0) {
+        if (S_final)
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S_final[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+        return;
+    }
 
-    constexpr int FULL = REC_LDS / 1024;          // whole 1 KB pieces
-    constexpr int REST = (REC_LDS % 1024) / 16;   // lanes of the partial piece
-    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)buf[0]);
-    auto stage = [&](int c) {
-        const char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES + lane * 16;
-        const uint32_t dst = lds0 + (uint32_t)((c & 1) * REC_LDS);
-#pragma unroll 4
-        for (int p = 0; p < FULL; ++p) lds_dma16(dst + p * 1024, rec + p * 1024);
-        if (REST > 0 && lane < REST) lds_dma16(dst + FULL * 1024, rec + FULL * 1024);
+    auto rec = [&](int c) -> const char* {
+        return ws + ((size_t)bh * nchunks + min(c, nchunks - 1)) * REC_BYTES;
     };
-    auto load_u0 = [&](int c, uint2 (&u)[4]) {
-        const char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES + REC_U0;
+    auto op = [&](const char* rp, int off) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(rp + off + lane * 16);
+    };
+    bf16x8 aW[16], aQ[16], aM[6], aK[16];
+    f32x4 al[8];
+    uint2 u0raw[4];
+    auto load_W = [&](const char* rp) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) aW[j] = op(rp, REC_NW + j * OPB);
 #pragma unroll
         for (int I = 0; I < 4; ++I)
-            u[I] = *reinterpret_cast<const uint2*>(rec + ((I * 8 + ct) * 64 + lane) * 8);
+            u0raw[I] = *reinterpret_cast<const uint2*>(rp + REC_U0 + ((I * 8 + ct) * 64 + lane) * 8);
     };
+    auto load_Q = [&](const char* rp) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) aQ[j] = op(rp, REC_QD + j * OPB);
+    };
+    auto load_MK = [&](const char* rp) {
+#pragma unroll
+        for (int j = 0; j < 6; ++j) aM[j] = op(rp, REC_M + j * OPB);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) aK[j] = op(rp, REC_KR + j * OPB);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) al[m] = *reinterpret_cast<const f32x4*>(rp + REC_AL + (16 * m + 4 * g) * 4);
+    };
+    load_W(rec(0));
+    load_Q(rec(0));
+    load_MK(rec(0));
 
-    uint2 u0raw[4];
-    f32x4 Oprev[4];
-    if (nchunks > 0) {
-        stage(0);
-        load_u0(0, u0raw);
-    }
     for (int c = 0; c < nchunks; ++c) {
-        // Everything issued so far has landed: this chunk's record and U0,
-        // and the previous chunk's output stores.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        f32x4 U0[4];
+        const char* rn = rec(c + 1);   // clamped: the last chunk reloads itself harmlessly
+        bf16x8 SB[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) SB[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
+        // U = U0 - W S
+        f32x4 accU[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const f32x2 lo = unpack2(u0raw[I].x), hi = unpack2(u0raw[I].y);
-            U0[I] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            accU[I] = f32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        if (c + 1 < nchunks) {
-            stage(c + 1);
-            load_u0(c + 1, u0raw);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) accU[I] = mma32(aW[I * 4 + kk], SB[kk], accU[I]);
+        load_W(rn);
+        bf16x8 UB[2];
+        UB[0] = pack8(accU[0], accU[1]);
+        UB[1] = pack8(accU[2], accU[3]);
+        // O = Q_decay S + M_qk U
+        f32x4 O[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) O[I] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) O[I] = mma32(aQ[I * 4 + kk], SB[kk], O[I]);
+        load_Q(rn);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) O[I] = mma32(aM[I], UB[0], O[I]);
+        O[2] = mma32(aM[4], UB[1], O[2]);
+        O[3] = mma32(aM[5], UB[1], O[3]);
+        // S = Diag(a_last) S + K_restore^T U
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            Sacc[m] *= al[m];
+            Sacc[m] = mma32(aK[2 * m], UB[0], Sacc[m]);
+            Sacc[m] = mma32(aK[2 * m + 1], UB[1], Sacc[m]);
         }
-        // the previous chunk's outputs leave now, behind this chunk's loads
-        if (c > 0) store_o(Oprev, o, ((size_t)b * T + (size_t)(c - 1) * C) * H + h, (size_t)H, ncol, C);
-        const char* sb = buf[c & 1];
-        state_pass<true>(Sacc, U0, reinterpret_cast<const bf16*>(sb + REC_NW),
-                   reinterpret_cast<const bf16*>(sb + REC_QD), reinterpret_cast<const bf16*>(sb + REC_M),
-                   reinterpret_cast<const bf16*>(sb + REC_KR), reinterpret_cast<const float*>(sb + REC_AL),
-                   Oprev);
-        // LDS reads of buf[c & 1] must finish before chunk c + 2 refills it
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        load_MK(rn);
+        store_o(O, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, ncol, T - c * C);
     }
-    if (nchunks > 0)
-        store_o(Oprev, o, ((size_t)b * T + (size_t)(nchunks - 1) * C) * H + h, (size_t)H, ncol,
-                T - (nchunks - 1) * C);
 
     if (S_final) {
 #pragma unroll

@@ -3,9 +3,11 @@
 
 One JSON line on stdout. The headline (``value``) is prefill tokens/s on the
 workload chosen with --workload (default: B=1, H=16, T=4096, d=128, chunk 64,
-bf16 q/k/v, fp32 state). A "step" is one full prefill of that batch (one
-launch of the fused kernel: chunk cumsum and decay scaling, intra-chunk Gram,
-UT inverse, pseudo-values, outputs and the state carry). Inputs are resident
+bf16 q/k/v, fp32 state). A "step" is one full prefill of that batch: one call
+of kda_prefill_fwd, i.e. chunk cumsum and decay scaling, intra-chunk Gram,
+UT inverse, pseudo-values, outputs and the state carry (for few heads a
+chunk-parallel prep launch followed by the state-walk launch; the roofline
+covers both, timed together with HIP events on their stream). Inputs are resident
 in HBM before timing; each timed step reads its own replica of the batch so
 the 256 MB last-level cache cannot hold the inputs between steps.
 
@@ -195,6 +197,9 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["prefill", "batched", "long"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
+                         "the HBM byte counters against a known traffic)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -209,6 +214,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 5}))
+        return
     kda.load_library()
     cfg = W.PREFILL_CONFIGS[args.workload]
     steps = args.steps
@@ -220,7 +234,11 @@ def main():
          f"{pre['tflops']:.1f} TFLOP/s")
 
     workload = cfg.describe()
-    traffic = measured_traffic("prefill_mfma", workload)
+    traffic = measured_traffic("prefill", workload)
+    if pre["workspace_bytes"] > 0:
+        kernels = "prefill_prep_kernel + prefill_state_kernel"
+    else:
+        kernels = "prefill_fused_kernel"
     result = {
         "metric": "KDA prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW",
         "value": pre["tokens_per_s"],
@@ -239,7 +257,7 @@ def main():
                    "input_replicas": pre["replicas"], "workspace_bytes": pre["workspace_bytes"]},
         "roofline": {"bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": pre["gbs"] / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": "prefill_mfma_kernel",
+                     "traffic": traffic, "kernel": kernels,
                      "kernel_us": pre["kernel_ms"] * 1e3, "algorithmic_bytes": pre["bytes"]},
         "mfma": {"flops_per_step": pre["flops"], "achieved_tflops": pre["tflops"],
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,

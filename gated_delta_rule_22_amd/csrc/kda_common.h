@@ -60,6 +60,13 @@ __device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Wave index inside the workgroup, as a wave-uniform (scalar) value. Control
+// flow that depends on it is then a scalar branch: MFMA instructions ignore
+// the EXEC mask, so they must never sit under a lane-masked branch.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Natural exponential through the hardware exp2 (v_exp_f32).
 __device__ __forceinline__ float exp_e(float x) { return __expf(x); }
 

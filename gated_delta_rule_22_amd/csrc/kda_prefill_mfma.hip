@@ -146,7 +146,7 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
 {
     constexpr int TPT = C / NW;
     constexpr int VPR = DVB / 8;   // 16-byte pieces per value row
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int t0 = wave * TPT;
     auto row = [&](int tok) -> size_t { return ((size_t)b * T + min(tok, T - 1)) * H + h; };
 #pragma unroll
@@ -173,7 +173,7 @@ __device__ __forceinline__ void stage1a(Prep& sm, bf16* sV, const Inputs<NW>& in
     constexpr int TPT = C / NW;
     constexpr int VPR = DVB / 8;
     constexpr int VS = DVB + 8;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int t0 = wave * TPT;
     f32x2 sum = {0.f, 0.f};
 #pragma unroll
@@ -193,7 +193,7 @@ template <int NW>
 __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok) {
     constexpr int TPT = C / NW;
     constexpr int SPB = NW / 4;      // token ranges per 16-token block
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int t0 = wave * TPT;
     const int blk = t0 >> 4;
     const int d0 = 2 * lane;
@@ -284,7 +284,7 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
 // inverts (I + L_II) in fp32 right away.
 template <int NW>
 __device__ __forceinline__ void stage2(Prep& sm) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
     // Work list per wave, 4 bits per pair index (15 = none), at most 3 pairs.
     // 8 waves: the diagonal blocks on waves 0-3 (each followed by its
@@ -357,7 +357,7 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
     constexpr int VS = DVB + 8;
     constexpr int NWT = 8 / NW;
     constexpr int NTILE = NWT + 1;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
 
     for (int idx = tid; idx < C * 64; idx += NW * 64) {
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     __shared__ Prep sm;
     __shared__ bf16 sV[C * (DVB + 8)];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
     const int vb = blockIdx.x % NVB;
     const int bh = blockIdx.x / NVB;
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     __shared__ Prep sm;
     __shared__ bf16 sV[C * (DVB + 8)];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int nchunks = (T + C - 1) / C;
     const int ngrp = (nchunks + cpw - 1) / cpw;
     const int bh = blockIdx.x / ngrp;
@@ -797,6 +797,12 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                int B, int T, int H, void* ws, hipStream_t st)
 {
     const long heads = (long)B * H;
+    if (heads >= 256) {
+        hipLaunchKernelGGL(prefill_fused_kernel<8>, dim3((unsigned)heads), dim3(512), 0, st,
+                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
+                           (bf16*)o, S_final, T, H, 1);
+        return hipGetLastError();
+    }
     if (heads >= kSplitBelowHeads) {
         hipLaunchKernelGGL(prefill_fused_kernel<4>, dim3((unsigned)(heads * 2)), dim3(256), 0, st,
                            (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,

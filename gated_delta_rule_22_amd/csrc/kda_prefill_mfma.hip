@@ -34,8 +34,11 @@
 //    chunk-head, -W, Q_decay, K_restore^T, M_qk (bf16, in MFMA operand
 //    register order), U0 and a_last to a workspace. The state
 //    kernel then walks the chunks in order doing only the three state
-//    passes, one wave per 16 value columns, loading each chunk's operands
-//    straight into MFMA registers while the previous chunk computes.
+//    passes, twelve waves per 16 value columns: four compute U, four
+//    update the state, four form the output rows; each loads only its
+//    operands, straight into MFMA registers, while the other passes run.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -649,130 +652,194 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     }
 }
 
-// State kernel: one wave per (batch*head, 16 value columns), no LDS and no
-// barriers. Each chunk's A operands arrive straight into registers from the
-// operand record (L2-resident: the 8 column waves of a head read the same
-// record and sit on the same XCD, block ids sharing id % 8). Every operand
-// set is reloaded for the next chunk right after its last use in this chunk,
-// so its loads overlap the rest of this chunk's MFMAs.
-__global__ __launch_bounds__(64, 1) void prefill_state_kernel(
+// State kernel: one workgroup of twelve waves per (batch*head, 16 value
+// columns). Each wave has one role, so the chunk-to-chunk chain is two short
+// MFMA passes and every wave loads only the few operands it uses:
+//   waves 0-3  (U): U = U0 - W S for token tile w                 (-W: 4 KB)
+//   waves 4-7  (S): S = Diag(a_last) S + K_restore^T U for state rows
+//                   32s .. 32s + 31, s = w - 4           (K_restore^T: 4 KB)
+//   waves 8-11 (O): O = Q_decay S + M_qk U for token tile w - 8
+// S (bf16, B-operand order) and U pass between waves through LDS, two
+// barriers per chunk: [S_c ready] U and Q_decay S; [U_c ready] S update and
+// M_qk U. Operands arrive straight into registers from the operand record,
+// which comes from HBM or the last-level cache: every wave keeps a ring of
+// PF operand sets and fetches several chunks ahead. A wave issues its
+// fetches in the phase where it is off the chain (one 1 KB load takes a wave
+// tens of cycles to issue): the S waves and output tiles 0, 1 in phase 1,
+// the U waves and output tiles 2, 3 in phase 2. The column tiles of a head
+// run on one XCD (block ids sharing id % 8) and share its L2. The U and S
+// waves run at raised priority so the output waves sharing their SIMDs do
+// not delay the chain.
+namespace mf {
+constexpr int PF = 4;   // operand sets in flight per wave
+}
+
+__global__ __launch_bounds__(768, 1) void prefill_state_kernel(
     const char* __restrict__ ws, const float* S0, bf16* __restrict__ o, float* S_final,
     int T, int H, int BH)
 {
     using namespace mf;
-    const int lane = threadIdx.x;
+    __shared__ bf16x8 sSB[4][64];        // S as four B operands (32-deep steps)
+    __shared__ bf16x4 sUB[2][64][2];     // U as two B operands, halves by token tile
+    __shared__ bf16 sO[4][16 * 16];      // output tiles, token-major
+
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
     const int grp = blockIdx.x >> 6;
     const int bh = grp * 8 + (blockIdx.x & 7);
     const int ct = (blockIdx.x >> 3) & 7;          // value column tile
-    if (bh >= BH) return;
+    if (bh >= BH) return;                          // whole workgroup: uniform
     const int b = bh / H, h = bh - b * H;
     const int ncol = 16 * ct + r;
     const int nchunks = (T + C - 1) / C;
-
-    f32x4 Sacc[8];
     const size_t sbase = (size_t)bh * DK * 128;
-    if (S0) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Sacc[m][i] = S0[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol];
-    } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) Sacc[m] = zero4();
-    }
-    if (nchunks == 0) {
-        if (S_final)
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S_final[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol] = Sacc[m][i];
-        return;
-    }
 
+    // record of chunk c, clamped: fetches past the end reload the last one
     auto rec = [&](int c) -> const char* {
         return ws + ((size_t)bh * nchunks + min(c, nchunks - 1)) * REC_BYTES;
     };
     auto op = [&](const char* rp, int off) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(rp + off + lane * 16);
     };
-    bf16x8 aW[16], aQ[16], aM[6], aK[16];
-    f32x4 al[8];
-    uint2 u0raw[4];
-    auto load_W = [&](const char* rp) {
+    // Runs step(set, prev, c, full) for every chunk with set = operand set
+    // c % PF and prev = set (c - 1) % PF, unrolled so that each set is a
+    // distinct register array. Whole groups of PF full chunks run unguarded
+    // (so the compiler can count the loads in flight across the loop); the
+    // remaining chunks follow, with `full` false for a chunk that may end
+    // before 64 tokens.
+    const int nfull = T / C;
+    auto walk = [&](auto& sets, auto&& step) {
+        int c = 0;
+        for (; c + PF <= nfull; c += PF) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) aW[j] = op(rp, REC_NW + j * OPB);
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-            u0raw[I] = *reinterpret_cast<const uint2*>(rp + REC_U0 + ((I * 8 + ct) * 64 + lane) * 8);
-    };
-    auto load_Q = [&](const char* rp) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) aQ[j] = op(rp, REC_QD + j * OPB);
-    };
-    auto load_MK = [&](const char* rp) {
-#pragma unroll
-        for (int j = 0; j < 6; ++j) aM[j] = op(rp, REC_M + j * OPB);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) aK[j] = op(rp, REC_KR + j * OPB);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) al[m] = *reinterpret_cast<const f32x4*>(rp + REC_AL + (16 * m + 4 * g) * 4);
-    };
-    load_W(rec(0));
-    load_Q(rec(0));
-    load_MK(rec(0));
-
-    for (int c = 0; c < nchunks; ++c) {
-        const char* rn = rec(c + 1);   // clamped: the last chunk reloads itself harmlessly
-        bf16x8 SB[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) SB[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
-        // U = U0 - W S
-        f32x4 accU[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const f32x2 lo = unpack2(u0raw[I].x), hi = unpack2(u0raw[I].y);
-            accU[I] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            for (int k = 0; k < PF; ++k) step(sets[k], sets[(k + PF - 1) % PF], c + k, std::true_type{});
         }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int I = 0; I < 4; ++I) accU[I] = mma32(aW[I * 4 + kk], SB[kk], accU[I]);
-        load_W(rn);
-        bf16x8 UB[2];
-        UB[0] = pack8(accU[0], accU[1]);
-        UB[1] = pack8(accU[2], accU[3]);
-        // O = Q_decay S + M_qk U
-        f32x4 O[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) O[I] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int I = 0; I < 4; ++I) O[I] = mma32(aQ[I * 4 + kk], SB[kk], O[I]);
-        load_Q(rn);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) O[I] = mma32(aM[I], UB[0], O[I]);
-        O[2] = mma32(aM[4], UB[1], O[2]);
-        O[3] = mma32(aM[5], UB[1], O[3]);
-        // S = Diag(a_last) S + K_restore^T U
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            Sacc[m] *= al[m];
-            Sacc[m] = mma32(aK[2 * m], UB[0], Sacc[m]);
-            Sacc[m] = mma32(aK[2 * m + 1], UB[1], Sacc[m]);
-        }
-        load_MK(rn);
-        store_o(O, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, ncol, T - c * C);
-    }
+        for (int k = 0; k < PF; ++k)
+            if (c + k < nchunks) step(sets[k], sets[(k + PF - 1) % PF], c + k, std::false_type{});
+    };
 
-    if (S_final) {
+    if (wave < 4) {
+        // ---- U = U0 - W S, token tile I (fetches in phase 2, PF ahead) ----
+        __builtin_amdgcn_s_setprio(2);
+        const int I = wave;
+        struct Ops { bf16x8 w[4]; uint2 u0; };
+        auto load = [&](Ops& x, int c) {
+            const char* rp = rec(c);
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+            for (int kk = 0; kk < 4; ++kk) x.w[kk] = op(rp, REC_NW + (I * 4 + kk) * OPB);
+            x.u0 = *reinterpret_cast<const uint2*>(rp + REC_U0 + ((I * 8 + ct) * 64 + lane) * 8);
+        };
+        Ops sets[PF];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S_final[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+        for (int k = 0; k < PF; ++k) load(sets[k], k);
+        walk(sets, [&](Ops& x, Ops&, int c, auto) {
+            lds_barrier();                                   // S_c ready
+            const f32x2 lo = unpack2(x.u0.x), hi = unpack2(x.u0.y);
+            f32x4 acc = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mma32(x.w[kk], sSB[kk][lane], acc);
+            sUB[I >> 1][lane][I & 1] = __builtin_convertvector(acc, bf16x4);
+            lds_barrier();                                   // U_c ready
+            load(x, c + PF);
+        });
+    } else if (wave < 8) {
+        // ---- S = Diag(a_last) S + K_restore^T U, state rows 32s .. 32s + 31
+        //      (fetches in phase 1, PF - 1 ahead) ----
+        __builtin_amdgcn_s_setprio(2);
+        const int s = wave - 4, m0 = 2 * s;
+        f32x4 Sacc[2];
+        if (S0) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Sacc[m][i] = S0[sbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol];
+        } else {
+            Sacc[0] = zero4();
+            Sacc[1] = zero4();
+        }
+        struct Ops { bf16x8 k[4]; f32x4 al[2]; };
+        auto load = [&](Ops& x, int c) {
+            const char* rp = rec(c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x.k[j] = op(rp, REC_KR + (2 * m0 + j) * OPB);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                x.al[m] = *reinterpret_cast<const f32x4*>(rp + REC_AL + (16 * (m0 + m) + 4 * g) * 4);
+        };
+        Ops sets[PF];
+#pragma unroll
+        for (int k = 0; k < PF - 1; ++k) load(sets[k], k);
+        sSB[s][lane] = pack8(Sacc[0], Sacc[1]);
+        walk(sets, [&](Ops& x, Ops& px, int c, auto) {
+            lds_barrier();                                   // S_c ready
+            Sacc[0] *= x.al[0];
+            Sacc[1] *= x.al[1];
+            load(px, c + PF - 1);
+            lds_barrier();                                   // U_c ready
+            const bf16x8 UB0 = *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]);
+            const bf16x8 UB1 = *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                Sacc[m] = mma32(x.k[2 * m], UB0, Sacc[m]);
+                Sacc[m] = mma32(x.k[2 * m + 1], UB1, Sacc[m]);
+            }
+            sSB[s][lane] = pack8(Sacc[0], Sacc[1]);
+        });
+        if (S_final) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S_final[sbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+        }
+    } else {
+        // ---- O = Q_decay S + M_qk U, token tile I ----
+        const int I = wave - 8;
+        // M_qk operands of row tile I: against U rows 0-31 (record entry I)
+        // and, for I >= 2, against U rows 32-63 (entry I + 2)
+        struct Ops { bf16x8 q[4]; bf16x8 m0, m1; };
+        auto load = [&](Ops& x, int c) {
+            const char* rp = rec(c);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) x.q[kk] = op(rp, REC_QD + (I * 4 + kk) * OPB);
+            x.m0 = op(rp, REC_M + I * OPB);
+            if (I >= 2) x.m1 = op(rp, REC_M + (I + 2) * OPB);
+        };
+        // the tile leaves through LDS so that each lane stores 4 columns of
+        // one token (8 bytes) instead of 4 tokens of one column
+        bf16* tile = sO[I];
+        const int tt = lane >> 2, tc = 4 * (lane & 3);
+        // separate loops for the two fetch phases, so that each has one
+        // load pattern the compiler can count across iterations
+        auto run = [&](auto early) {
+            constexpr bool kEarly = decltype(early)::value;   // fetch in phase 1
+            Ops sets[PF];
+#pragma unroll
+            for (int k = 0; k < PF - 1; ++k) load(sets[k], k);
+            if (!kEarly) load(sets[PF - 1], PF - 1);
+            walk(sets, [&](Ops& x, Ops& px, int c, auto full) {
+                lds_barrier();                               // S_c ready
+                f32x4 O = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) O = mma32(x.q[kk], sSB[kk][lane], O);
+                if (kEarly) load(px, c + PF - 1);
+                lds_barrier();                               // U_c ready
+                O = mma32(x.m0, *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]), O);
+                if (I >= 2) O = mma32(x.m1, *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]), O);
+                if (!kEarly) load(x, c + PF);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tile[(4 * g + e) * 16 + r] = (bf16)O[e];
+                lds_fence_wave();
+                const uint2 v = *reinterpret_cast<const uint2*>(&tile[tt * 16 + tc]);
+                const int t = 16 * I + tt;
+                if (decltype(full)::value || t < T - c * C)
+                    *reinterpret_cast<uint2*>(o + (((size_t)b * T + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc) = v;
+            });
+        };
+        if (I < 2) run(std::true_type{});
+        else run(std::false_type{});
     }
 }
 
@@ -821,7 +888,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long groups = (heads + 7) / 8;   // 8 heads x 8 column tiles per group of 64 blocks
-    hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)(groups * 64)), dim3(64), 0, st,
+    hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)(groups * 64)), dim3(768), 0, st,
                        (const char*)ws, S0, (bf16*)o, S_final, T, H, (int)heads);
     return hipGetLastError();
 }

@@ -14,13 +14,17 @@
 //    forward substitution over four 16-token blocks (fp32 inverses of the
 //    16x16 diagonal blocks, bf16 MFMA elsewhere). Only three MFMA passes then
 //    depend on the state: U, then O and S_out.
-//  * Decay factors never overflow. With b_t the decay accumulated from the
-//    start of t's 16-token block to t, the Gram entry for t in block I and s
-//    in block J <= I is  sum_d (k_t b_t)[d] (k_s / b_s)[d] G_IJ[d],  G_IJ the
-//    decay over blocks J..I-1 (1 on the diagonal). Every factor is <= 1
-//    except 1/b_s <= exp(80) for log-decays in [-5, 0] (the bound on the
-//    trillion-scale architecture page, section 4), inside fp32/bf16 range.
-//    K_decay, Q_decay and K_restore are likewise products of factors <= 1.
+//  * Decay factors never overflow. In a chunk whose every 8-token range
+//    decays by at most exp(-8) per channel (all but extreme inputs), the Gram
+//    entry for key s <= query t is  sum_d (k_t a_t)[d] (k_s / a_s)[d]  with a
+//    the decay from the chunk start: 1/a_s <= exp(64). Otherwise the chunk
+//    takes the 16-token block factorisation: with b_t the decay from the
+//    start of t's block, the entry for t in block I and s in block J <= I is
+//    sum_d (k_t b_t)[d] (k_s / b_s)[d] G_IJ[d], G_IJ the decay over blocks
+//    J..I-1 (1 on the diagonal); every factor is <= 1 except 1/b_s <=
+//    exp(80) for log-decays in [-5, 0] (the bound on the trillion-scale
+//    architecture page, section 4). Both stay inside fp32/bf16 range, and
+//    K_decay, Q_decay and K_restore are products of factors <= 1.
 //
 // Kernels:
 //  * fused_kernel: one workgroup per (batch*head, 16*NW value columns); walks
@@ -50,6 +54,10 @@ constexpr int C = 64;
 constexpr int KS = 136;            // padded row stride (bf16) of [64][128] tiles
 constexpr int TS = 72;             // padded row stride (bf16) of [*][64] tiles
 constexpr int LDT = 16 * 16 + 4;   // fp32 stride of one transposed diagonal L block
+// A chunk whose token ranges all decay by at most exp(-kRangeDecay) per
+// channel uses the chunk-level decay reference (1/a <= exp(8 * kRangeDecay)).
+constexpr float kRangeDecay = 8.f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -62,15 +70,17 @@ struct Prep {
     bf16 Ki[C * KS];     // k_s / b_s                Gram right; then -W in place
     bf16 KrT[DK * TS];   // K_restore^T [channel][token]
     bf16 RkT[DK * TS];   // (Diag(beta) K_decay)^T [channel][token]: substitution input
-    bf16 nL[C * TS];     // -L (upper blocks stay zero)
-    bf16 M[C * TS];      // M_qk (upper blocks stay zero)
-    float LdT[4 * LDT];  // diagonal blocks of L, fp32, transposed [s][t]
-    bf16 D[4 * 256];     // (I + L_II)^{-1}
+    bf16x8 NWop[16][64]; // -W as A operands (I, kk), operand-record order
+    bf16x8 Mop[6][64];   // M_qk as A operands (0,0),(1,0),(2,0),(3,0),(2,1),(3,1)
+    bf16x4 NLt[6][64];   // -L_IJ, J < I, as 16x16x16 A operands, pair I(I-1)/2 + J
+    bf16x4 Dt[4][64];    // (I + L_II)^{-1} as 16x16x16 A operands
+    float Lt[4 * LDT];   // diagonal blocks of L, fp32, [s][t]
     float P[4 * DK];     // decay from the chunk start to the start of block I
     float G[6 * DK];     // decay over blocks J..I-1 for the 6 pairs J < I
     float alast[DK];     // decay over the whole chunk
     float Tot[8 * DK];   // log-decay sums of the 8-or-4 token ranges
     float beta[C];
+    int strong[8];       // per token range: some channel decays by more than kRangeDecay
 };
 
 // Operand record written by the prep kernel, read by the state kernel, in
@@ -170,7 +180,8 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
 
 // Stage 1a: per-range log-decay sums; values and beta to LDS. Tokens at or
 // past ntok are padding: zero decay, value and beta (exact, the recurrence
-// leaves the state unchanged for them).
+// leaves the state unchanged for them). Each range also records whether some
+// channel decays by more than kRangeDecay over it.
 template <int NW, int DVB>
 __device__ __forceinline__ void stage1a(Prep& sm, bf16* sV, const Inputs<NW>& in, int ntok) {
     constexpr int TPT = C / NW;
@@ -182,6 +193,8 @@ __device__ __forceinline__ void stage1a(Prep& sm, bf16* sV, const Inputs<NW>& in
 #pragma unroll
     for (int j = 0; j < TPT; ++j) sum += (t0 + j < ntok) ? in.la[j] : f32x2{0.f, 0.f};
     *reinterpret_cast<f32x2*>(&sm.Tot[wave * DK + 2 * lane]) = sum;
+    const bool strong = __builtin_amdgcn_ballot_w64(fminf(sum[0], sum[1]) < -kRangeDecay) != 0;
+    if (lane == 0) sm.strong[wave] = strong;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int piece = tid + p * NW * 64;
@@ -191,9 +204,21 @@ __device__ __forceinline__ void stage1a(Prep& sm, bf16* sV, const Inputs<NW>& in
     if (tid < C) sm.beta[tid] = (tid < ntok) ? in.beta : 0.f;
 }
 
-// Stage 1b: decay-scaled operands. Thread (range = wave, channels 2*lane, +1).
+// True when no token range of the chunk has a strongly decaying channel:
+// the chunk then uses the chunk-level decay reference. Wave-uniform.
 template <int NW>
-__device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok) {
+__device__ __forceinline__ bool chunk_is_mild(const Prep& sm) {
+    int any = 0;
+#pragma unroll
+    for (int s = 0; s < NW; ++s) any |= sm.strong[s];
+    return __builtin_amdgcn_readfirstlane(any) == 0;
+}
+
+// Stage 1b: decay-scaled operands. Thread (range = wave, channels 2*lane, +1).
+// The decay reference is the chunk start when `fast`, else the start of the
+// token's 16-token block. FULL: every token of the chunk is real.
+template <int NW, bool FULL>
+__device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok, bool fast) {
     constexpr int TPT = C / NW;
     constexpr int SPB = NW / 4;      // token ranges per 16-token block
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -202,7 +227,8 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
     const int d0 = 2 * lane;
 
     f32x2 tau[4];                    // per-block log-decay totals, both channels
-    f32x2 off = {0.f, 0.f};          // log-decay from the block start to this range
+    f32x2 offb = {0.f, 0.f};         // log-decay from the block start to this range
+    f32x2 offc = {0.f, 0.f};         // log-decay from the chunk start to this range
 #pragma unroll
     for (int m = 0; m < 4; ++m) tau[m] = f32x2{0.f, 0.f};
 #pragma unroll
@@ -210,18 +236,18 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
         const float2 v = *reinterpret_cast<const float2*>(&sm.Tot[s * DK + d0]);
         const f32x2 vv = {v.x, v.y};
         tau[s / SPB] += vv;
-        if (s / SPB == blk && s < wave) off += vv;
+        if (s < wave) offc += vv;
+        if (s / SPB == blk && s < wave) offb += vv;
     }
-    // decay from the start of this block to the chunk end (K_restore factor)
-    f32x2 tail = {0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) if (m >= blk) tail += tau[m];
-    const f32x2 eR = {exp_e(tail[0]), exp_e(tail[1])};
-    // decay from the chunk start to the start of this block (K_decay factor)
-    f32x2 head = {0.f, 0.f};
+    const f32x2 all = tau[0] + tau[1] + tau[2] + tau[3];
+    f32x2 head = {0.f, 0.f};         // chunk start to the start of this block
 #pragma unroll
     for (int m = 0; m < 4; ++m) if (m < blk) head += tau[m];
-    const f32x2 eP = {exp_e(head[0]), exp_e(head[1])};
+    // K_restore factor: decay from the reference point to the chunk end;
+    // Diag(beta) K_decay factor: decay from the chunk start to the reference
+    const f32x2 tail = fast ? all : all - head;
+    const f32x2 eR = {exp_e(tail[0]), exp_e(tail[1])};
+    const f32x2 eP = fast ? f32x2{1.f, 1.f} : f32x2{exp_e(head[0]), exp_e(head[1])};
 
     // chunk-level factors, spread over the first four token ranges
     if (wave == 0) {
@@ -244,19 +270,20 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
             *reinterpret_cast<float2*>(&sm.G[pidx * DK + d0]) = make_float2(exp_e(sum[0]), exp_e(sum[1]));
         }
     } else if (wave == 3) {
-        const f32x2 all = tau[0] + tau[1] + tau[2] + tau[3];
         *reinterpret_cast<float2*>(&sm.alast[d0]) = make_float2(exp_e(all[0]), exp_e(all[1]));
     }
 
-    f32x2 run = off;
+    // running log2-decay from the reference point; b_t = 2^run, 1/b_t = 2^-run
+    f32x2 run = (fast ? offc : offb) * kLog2e;
     float kr0[TPT], kr1[TPT], rk0[TPT], rk1[TPT];
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
         const int t = t0 + j;
-        const bool ok = t < ntok;
-        run += ok ? in.la[j] : f32x2{0.f, 0.f};
-        const f32x2 bt = {exp_e(run[0]), exp_e(run[1])};     // <= 1
-        const f32x2 ib = {exp_e(-run[0]), exp_e(-run[1])};   // <= exp(80) in range
+        const bool ok = FULL || t < ntok;
+        const f32x2 la = ok ? in.la[j] : f32x2{0.f, 0.f};
+        run = la * kLog2e + run;
+        const f32x2 bt = {__builtin_amdgcn_exp2f(run[0]), __builtin_amdgcn_exp2f(run[1])};    // <= 1
+        const f32x2 ib = {__builtin_amdgcn_exp2f(-run[0]), __builtin_amdgcn_exp2f(-run[1])};  // bounded above
         const f32x2 kk = ok ? unpack2(in.k[j]) : f32x2{0.f, 0.f};
         const f32x2 qq = ok ? unpack2(in.q[j]) : f32x2{0.f, 0.f};
         const f32x2 kd = kk * bt;
@@ -283,10 +310,16 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
     }
 }
 
-// Stage 2: Gram blocks -> -L, M_qk; the wave owning a diagonal block also
-// inverts (I + L_II) in fp32 right away.
+// Stage 2: Gram blocks -> -L, M_qk, computed transposed: for the pair (I, J),
+// J <= I, A = K_inv rows of block J (times G_IJ off the diagonal, block
+// reference only) and B =
+// K_decay or Q_decay rows of block I leave lane (g, r) holding the entries
+// (t = 16I + r, s = 16J + 4g + i): row r of the block, which is the A
+// operand of a 16x16x16 step and one half of a 16x16x32 one, so each block
+// is stored with a single 8-byte write per lane. The wave owning a diagonal
+// block then forms rows of (I + L_II)^{-1} in fp32.
 template <int NW>
-__device__ __forceinline__ void stage2(Prep& sm) {
+__device__ __forceinline__ void stage2(Prep& sm, bool fast) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
     // Work list per wave, 4 bits per pair index (15 = none), at most 3 pairs.
@@ -303,67 +336,79 @@ __device__ __forceinline__ void stage2(Prep& sm) {
         if (p == 15) break;
         const int I = (kPairI >> (2 * p)) & 3, J = (kPairJ >> (2 * p)) & 3;
         const bool diag = I == J;
-        const bf16* rp = sm.Ki + (16 * J + r) * KS + 8 * g;
-        bf16x8 Bk[4];
+        const bf16* ap = sm.Ki + (16 * J + r) * KS + 8 * g;
+        bf16x8 Ak[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) Bk[kk] = ld8(rp + 32 * kk);
-        if (!diag) {
+        for (int kk = 0; kk < 4; ++kk) Ak[kk] = ld8(ap + 32 * kk);
+        if (!diag && !fast) {
             const float* gp = sm.G + (I * (I - 1) / 2 + J) * DK + 8 * g;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                Bk[kk] = scale8(Bk[kk], *reinterpret_cast<const f32x4*>(gp + 32 * kk),
+                Ak[kk] = scale8(Ak[kk], *reinterpret_cast<const f32x4*>(gp + 32 * kk),
                                 *reinterpret_cast<const f32x4*>(gp + 32 * kk + 4));
         }
         const bf16* kp = sm.Kd + (16 * I + r) * KS + 8 * g;
         const bf16* qp = sm.Qd + (16 * I + r) * KS + 8 * g;
+        const float bt = sm.beta[16 * I + r];
         f32x4 aK = zero4(), aQ = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            aK = mma32(ld8(kp + 32 * kk), Bk[kk], aK);
-            aQ = mma32(ld8(qp + 32 * kk), Bk[kk], aQ);
+            aK = mma32(Ak[kk], ld8(kp + 32 * kk), aK);
+            aQ = mma32(Ak[kk], ld8(qp + 32 * kk), aQ);
         }
-        const int s = 16 * J + r;
-        f32x4 lv;
+        f32x4 lv, mv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int tl = 4 * g + i;              // row inside block I
-            const int t = 16 * I + tl;
-            lv[i] = (!diag || r < tl) ? sm.beta[t] * aK[i] : 0.f;
-            const float mv = (!diag || r <= tl) ? aQ[i] : 0.f;
-            sm.nL[t * TS + s] = (bf16)(-lv[i]);
-            sm.M[t * TS + s] = (bf16)mv;
+            const int s = 4 * g + i;                 // key token inside block J
+            lv[i] = (!diag || s < r) ? bt * aK[i] : 0.f;
+            mv[i] = (!diag || s <= r) ? aQ[i] : 0.f;
         }
-        if (diag) {
-            float* Lt = sm.LdT + I * LDT;
-            *reinterpret_cast<f32x4*>(&Lt[r * 16 + 4 * g]) = lv;
+        // M_qk operand (I, J / 2) takes this block as its half J % 2; the
+        // halves above the diagonal, (0, 1) and (2, 3), are zero
+        bf16x4* mop = reinterpret_cast<bf16x4*>(&sm.Mop[(J < 2) ? I : I + 2][lane]);
+        mop[J & 1] = __builtin_convertvector(mv, bf16x4);
+        if (diag && (I & 1) == 0) mop[1] = bf16x4{};
+        if (!diag) {
+            sm.NLt[I * (I - 1) / 2 + J][lane] = __builtin_convertvector(-lv, bf16x4);
+        } else {
+            float* Lt = sm.Lt + I * LDT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Lt[(4 * g + i) * 16 + r] = lv[i];   // [s][t]
             lds_fence_wave();
-            // column r of (I + L_II)^{-1}, right-looking substitution
-            float x[16];
+            // row r of (I + L)^{-1}: y (I + L) = e_r, backward over columns j,
+            // y_j = [j == r] - sum_{i > j} y_i L[i][j]  (zero for j > r)
+            float y[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i == r) ? 1.f : 0.f;
+            for (int j = 15; j >= 0; --j) {
+                float acc = (j == r) ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < 15; ++m) {
-#pragma unroll
-                for (int i = m + 1; i < 16; ++i) x[i] -= Lt[m * 16 + i] * x[m];
+                for (int i = j + 1; i < 16; ++i) acc -= y[i] * Lt[j * 16 + i];
+                y[j] = acc;
             }
+            f32x4 d;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if ((i >> 2) == g) sm.D[I * 256 + i * 16 + r] = (bf16)x[i];
+            for (int i = 0; i < 4; ++i)
+                d[i] = (g == 0) ? y[i] : (g == 1) ? y[4 + i] : (g == 2) ? y[8 + i] : y[12 + i];
+            sm.Dt[I][lane] = __builtin_convertvector(d, bf16x4);
         }
     }
 }
 
-// Stage 3: Q_decay in place; forward substitution for -W (into Ki) and U0.
+// Stage 3: Q_decay in place (block reference only: with the chunk reference
+// Qd already is Q_decay); forward substitution for -W and U0.
 // Tiles: W channel tiles wave, wave + NW (< 8), then the U0 tile at u0col.
+// Block I: Y_I -= sum_{J<I} L_IJ X_J, then X_I = D_I Y_I (accumulator order,
+// feeds later blocks as the B operand) and, for W, X_I^T = Y_I^T D_I^T: its
+// accumulator holds W rows in A-operand order, stored straight into NWop.
 template <int NW, int DVB>
-__device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x4 (&U0)[4]) {
+__device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x4 (&U0)[4], bool fast) {
     constexpr int VS = DVB + 8;
     constexpr int NWT = 8 / NW;
     constexpr int NTILE = NWT + 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
 
-    for (int idx = tid; idx < C * 64; idx += NW * 64) {
+    for (int idx = tid; !fast && idx < C * 64; idx += NW * 64) {
         const int t = idx >> 6, d = 2 * (idx & 63);
         uint32_t* p = reinterpret_cast<uint32_t*>(&sm.Qd[t * KS + d]);
         const f32x2 a = unpack2(*p);
@@ -390,21 +435,22 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
         }
 #pragma unroll
         for (int J = 0; J < I; ++J) {
-            const s16x4 a = ld4(sm.nL + (16 * I + r) * TS + 16 * J + 4 * g);
+            const s16x4 a = __builtin_bit_cast(s16x4, sm.NLt[I * (I - 1) / 2 + J][lane]);
 #pragma unroll
             for (int tl = 0; tl < NTILE; ++tl) Y[tl] = mma16(a, pack4(X[tl][J]), Y[tl]);
         }
-        const s16x4 dI = ld4(sm.D + I * 256 + r * 16 + 4 * g);
+        const s16x4 dI = __builtin_bit_cast(s16x4, sm.Dt[I][lane]);
 #pragma unroll
-        for (int tl = 0; tl < NTILE; ++tl) X[tl][I] = mma16(dI, pack4(Y[tl]), zero4());
-    }
-#pragma unroll
-    for (int tl = 0; tl < NWT; ++tl) {
-        const int d = 16 * (wave + tl * NW) + r;
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.Ki[(16 * I + 4 * g + i) * KS + d] = (bf16)(-X[tl][I][i]);
+        for (int tl = 0; tl < NTILE; ++tl) {
+            const s16x4 yb = pack4(Y[tl]);
+            X[tl][I] = mma16(dI, yb, zero4());
+            if (tl < NWT) {
+                const f32x4 xt = mma16(yb, dI, zero4());
+                const int dt = wave + tl * NW;                // channel tile
+                reinterpret_cast<bf16x4*>(&sm.NWop[I * 4 + (dt >> 1)][lane])[dt & 1] =
+                    __builtin_convertvector(-xt, bf16x4);
+            }
+        }
     }
 #pragma unroll
     for (int I = 0; I < 4; ++I) U0[I] = X[NWT][I];
@@ -422,8 +468,9 @@ struct NoOp { __device__ void operator()(int) const {} };
 
 template <bool PRELOAD, typename Between = NoOp>
 __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4],
-                                           const bf16* nW, const bf16* Qdec, const bf16* M,
-                                           const bf16* KrT, const float* alast, f32x4 (&O)[4],
+                                           const bf16x8 (*nW)[64], const bf16* Qdec,
+                                           const bf16x8 (*M)[64], const bf16* KrT,
+                                           const float* alast, f32x4 (&O)[4],
                                            Between between = Between())
 {
     const int lane = threadIdx.x & 63;
@@ -444,7 +491,7 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
         for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                aW[I][kk] = ldA_perm(nW + (16 * I + r) * KS, 32 * kk, g);
+                aW[I][kk] = nW[I * 4 + kk][lane];
                 aQ[I][kk] = ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g);
             }
         __builtin_amdgcn_sched_barrier(0);
@@ -464,7 +511,7 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
         for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                accU[I] = mma32(ldA_perm(nW + (16 * I + r) * KS, 32 * kk, g), SB[kk], accU[I]);
+                accU[I] = mma32(nW[I * 4 + kk][lane], SB[kk], accU[I]);
                 O[I] = mma32(ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g), SB[kk], O[I]);
             }
     }
@@ -473,9 +520,9 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
     UB[1] = pack8(accU[2], accU[3]);
 
 #pragma unroll
-    for (int I = 0; I < 4; ++I) O[I] = mma32(ldA_perm(M + (16 * I + r) * TS, 0, g), UB[0], O[I]);
-    O[2] = mma32(ldA_perm(M + (16 * 2 + r) * TS, 32, g), UB[1], O[2]);
-    O[3] = mma32(ldA_perm(M + (16 * 3 + r) * TS, 32, g), UB[1], O[3]);
+    for (int I = 0; I < 4; ++I) O[I] = mma32(M[I][lane], UB[0], O[I]);
+    O[2] = mma32(M[4][lane], UB[1], O[2]);
+    O[3] = mma32(M[5][lane], UB[1], O[3]);
     if (PRELOAD) {
         bf16x8 aK[8][2];
         f32x4 al[8];
@@ -539,8 +586,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const int col0 = vb * DVB;
     const int ncol = col0 + 16 * wave + r;
 
-    for (int i = tid; i < C * TS; i += NW * 64) { sm.nL[i] = (bf16)0.f; sm.M[i] = (bf16)0.f; }
-
     f32x4 Sacc[8];
     const size_t sbase = (size_t)bh * DK * 128;
     if (S0) {
@@ -558,19 +603,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     if (nchunks > 0) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, 0, col0);
 
     for (int c = 0; c < nchunks; ++c) {
+        const int ntok = T - c * C;
         lds_barrier();
-        stage1a<NW, DVB>(sm, sV, in, T - c * C);
+        stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
-        stage1b<NW>(sm, in, T - c * C);
+        const bool fast = chunk_is_mild<NW>(sm);
+        // (the 8-wave kernel keeps one masked variant: two would not fit its registers)
+        if (NW < 8 && ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
+        else stage1b<NW, false>(sm, in, ntok, fast);
         if (c + 1 < nchunks) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
         lds_barrier();
-        stage2<NW>(sm);
+        stage2<NW>(sm, fast);
         lds_barrier();
         f32x4 U0[4];
-        stage3<NW, DVB>(sm, sV, 16 * wave, U0);
+        stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
         lds_barrier();
         f32x4 O[4];
-        state_pass<(NW < 8)>(Sacc, U0, sm.Ki, sm.Qd, sm.M, sm.KrT, sm.alast, O);
+        state_pass<(NW < 8)>(Sacc, U0, sm.NWop, sm.Qd, sm.Mop, sm.KrT, sm.alast, O);
         store_o(O, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, ncol, T - c * C);
     }
 
@@ -602,42 +651,41 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     const int c1 = min(c0 + cpw, nchunks);
     const int b = bh / H, h = bh - b * H;
 
-    for (int i = tid; i < C * TS; i += NW * 64) { sm.nL[i] = (bf16)0.f; sm.M[i] = (bf16)0.f; }
-
     Inputs<NW> in;
     if (c0 < c1) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c0, 0);
     for (int c = c0; c < c1; ++c) {
+        const int ntok = T - c * C;
         lds_barrier();
-        stage1a<NW, DVB>(sm, sV, in, T - c * C);
+        stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
-        stage1b<NW>(sm, in, T - c * C);
+        const bool fast = chunk_is_mild<NW>(sm);
+        if (ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
+        else stage1b<NW, false>(sm, in, ntok, fast);
         if (c + 1 < c1) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
         lds_barrier();
-        stage2<NW>(sm);
+        stage2<NW>(sm, fast);
         lds_barrier();
         f32x4 U0[4];
-        stage3<NW, DVB>(sm, sV, 16 * wave, U0);
+        stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
         lds_barrier();
         char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
         // 54 A operands, spread over the waves: 16 B per lane each
         for (int j = wave; j < 54; j += NW) {
-            const bf16* rowp;
-            int k0, off;
+            bf16x8 val;
+            int off;
             if (j < 16) {              // -W (I = j / 4, kk = j % 4)
-                rowp = sm.Ki + (16 * (j >> 2) + r) * KS; k0 = 32 * (j & 3); off = REC_NW + j * OPB;
+                val = sm.NWop[j][lane]; off = REC_NW + j * OPB;
             } else if (j < 32) {       // Q_decay
                 const int jj = j - 16;
-                rowp = sm.Qd + (16 * (jj >> 2) + r) * KS; k0 = 32 * (jj & 3); off = REC_QD + jj * OPB;
+                val = ldA_perm(sm.Qd + (16 * (jj >> 2) + r) * KS, 32 * (jj & 3), g); off = REC_QD + jj * OPB;
             } else if (j < 38) {       // M_qk
-                const int jj = j - 32;
-                const int I = jj < 4 ? jj : jj - 2, kk = jj < 4 ? 0 : 1;
-                rowp = sm.M + (16 * I + r) * TS; k0 = 32 * kk; off = REC_M + jj * OPB;
+                val = sm.Mop[j - 32][lane]; off = REC_M + (j - 32) * OPB;
             } else {                   // K_restore^T (m = jj / 2, kk = jj % 2)
                 const int jj = j - 38;
-                rowp = sm.KrT + (16 * (jj >> 1) + r) * TS; k0 = 32 * (jj & 1); off = REC_KR + jj * OPB;
+                val = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g); off = REC_KR + jj * OPB;
             }
-            *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = ldA_perm(rowp, k0, g);
+            *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = val;
         }
         if (tid < DK / 4)
             *reinterpret_cast<f32x4*>(rec + REC_AL + tid * 16) = *reinterpret_cast<const f32x4*>(&sm.alast[4 * tid]);

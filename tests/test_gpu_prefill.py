@@ -234,6 +234,26 @@ def test_strong_decay_at_bound():
     report("log-decay in [-5,-4]", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
+@pytest.mark.parametrize("B,H", [(1, 2), (2, 64), (4, 64)])
+def test_decay_regime_changes_between_chunks(B, H):
+    # Mild decay, except one channel that drops by e^-12 over tokens 72-79
+    # (chunk 1) and by e^-16 over tokens 192-199 (the ragged last chunk):
+    # those chunks take the 16-token block factorisation, the others the
+    # chunk-level decay reference. Few heads (prep + state kernels) and
+    # many heads (both fused variants).
+    c = W.PREFILL_CONFIGS["prefill"]
+    x = W.prefill_inputs(c, B=B, T=200, H=H)
+    x["log_alpha"][:, 72:80, :, 5] = -1.5
+    x["log_alpha"][:, 192:200, :, 7] = -2.0
+    o, S = gpu_prefill(to_dev(x))
+    if B * H > 8:   # oracle on a few heads
+        idx = [0, H // 2, H - 1]
+        x = {k: (None if v is None else v[:1, :, idx]) for k, v in x.items()}
+        o, S = o[:1, :, idx], S[:1, idx]
+    ro, rS = oracle_prefill(x)
+    report(f"decay regimes B{B} H{H} T200", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
 def test_basis_keys_store_and_retrieve():
     # alpha = 1, beta = 1, S0 = 0, keys are signed basis vectors (exact in bf16):
     # the final state maps every key back to its value.

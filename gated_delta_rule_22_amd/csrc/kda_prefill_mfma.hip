@@ -550,17 +550,27 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
 }
 
 // Store a 64 x 16 output tile (accumulator layout) as bf16, tokens < ntok.
-__device__ __forceinline__ void store_o(const f32x4 (&O)[4], bf16* __restrict__ o, size_t row0,
-                                        size_t rstride, int ncol, int ntok) {
+// The tile goes through `stage` (this wave's 64 x 24 bf16 slot of an LDS
+// buffer that is dead during the state pass) so that each lane stores one
+// token's 16 columns with two 16-byte stores. Lanes past ntok store a copy of
+// the last real token's row to that row (same data, same address), so every
+// lane stores and the compiler sees a fixed number of stores.
+constexpr int OTS = 24;   // staging row stride (bf16): 16-byte aligned, conflict-free reads
+__device__ __forceinline__ void store_o(const f32x4 (&O)[4], bf16* stage, bf16* __restrict__ o,
+                                        size_t row0, size_t rstride, int col0, int ntok) {
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;
+    const int g = lane >> 4, r = lane & 15;
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * I + 4 * g + i;
-            if (t < ntok) o[(row0 + (size_t)t * rstride) * 128 + ncol] = (bf16)O[I][i];
-        }
+        for (int i = 0; i < 4; ++i) stage[(16 * I + 4 * g + i) * OTS + r] = (bf16)O[I][i];
+    lds_fence_wave();
+    const int t = min(lane, ntok - 1);
+    const uint4 lo = *reinterpret_cast<const uint4*>(&stage[t * OTS]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&stage[t * OTS + 8]);
+    bf16* dst = o + (row0 + (size_t)t * rstride) * 128 + col0;
+    *reinterpret_cast<uint4*>(dst) = lo;
+    *reinterpret_cast<uint4*>(dst + 8) = hi;
 }
 
 }  // namespace mf
@@ -608,8 +618,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
         const bool fast = chunk_is_mild<NW>(sm);
-        // (the 8-wave kernel keeps one masked variant: two would not fit its registers)
-        if (NW < 8 && ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
+        if (ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
         else stage1b<NW, false>(sm, in, ntok, fast);
         if (c + 1 < nchunks) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
         lds_barrier();
@@ -620,7 +629,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         lds_barrier();
         f32x4 O[4];
         state_pass<(NW < 8)>(Sacc, U0, sm.NWop, sm.Qd, sm.Mop, sm.KrT, sm.alast, O);
-        store_o(O, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, ncol, T - c * C);
+        // staging slots: waves 0-4 in Kd, 5-7 in Ki (both dead until the next chunk)
+        bf16* stage = (wave < 5) ? sm.Kd + wave * (C * OTS) : sm.Ki + (wave - 5) * (C * OTS);
+        store_o(O, stage, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, col0 + 16 * wave, ntok);
     }
 
     if (S_final) {
@@ -670,8 +681,12 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         lds_barrier();
         char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
-        // 54 A operands, spread over the waves: 16 B per lane each
-        for (int j = wave; j < 54; j += NW) {
+        // 54 A operands, spread over the waves: 16 B per lane each. Seven per
+        // wave; waves 6, 7 store their sixth operand twice (same data, same
+        // address) so that every wave issues a fixed number of stores.
+#pragma unroll
+        for (int jj = 0; jj < 7; ++jj) {
+            const int j = (wave + NW * jj < 54) ? wave + NW * jj : wave + NW * (jj - 1);
             bf16x8 val;
             int off;
             if (j < 16) {              // -W (I = j / 4, kk = j % 4)
@@ -687,8 +702,9 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
             }
             *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = val;
         }
-        if (tid < DK / 4)
-            *reinterpret_cast<f32x4*>(rec + REC_AL + tid * 16) = *reinterpret_cast<const f32x4*>(&sm.alast[4 * tid]);
+        if (wave == 0)   // lanes 32-63 repeat lanes 0-31
+            *reinterpret_cast<f32x4*>(rec + REC_AL + (lane & 31) * 16) =
+                *reinterpret_cast<const f32x4*>(&sm.alast[4 * (lane & 31)]);
         // U0 tile (I, wave) in accumulator order: 4 bf16 per lane
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -880,10 +896,15 @@ __global__ __launch_bounds__(768, 1) void prefill_state_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tile[(4 * g + e) * 16 + r] = (bf16)O[e];
                 lds_fence_wave();
-                const uint2 v = *reinterpret_cast<const uint2*>(&tile[tt * 16 + tc]);
-                const int t = 16 * I + tt;
-                if (decltype(full)::value || t < T - c * C)
+                // In a ragged last chunk, rows past the sequence end repeat the
+                // tile's last real row (same data, same address); a tile wholly
+                // past the end stores nothing. Full chunks store unconditionally.
+                const int nt = T - c * C;
+                if (decltype(full)::value || 16 * I < nt) {
+                    const int t = decltype(full)::value ? 16 * I + tt : min(16 * I + tt, nt - 1);
+                    const uint2 v = *reinterpret_cast<const uint2*>(&tile[(t - 16 * I) * 16 + tc]);
                     *reinterpret_cast<uint2*>(o + (((size_t)b * T + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc) = v;
+                }
             });
         };
         if (I < 2) run(std::true_type{});

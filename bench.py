@@ -161,7 +161,7 @@ def bench_decode(cfg, loops=2):
                 flops_per_step=A.decode_step_flops(cfg.B, cfg.H, cfg.dk, cfg.dv))
 
 
-def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18):
+def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18, min_seconds=10.0):
     """fp64 oracle on the host cores over a bounded sample of the same
     workload: whole heads (one per thread) over the first tokens of the
     sequence. Inputs are converted before the clock starts."""
@@ -178,14 +178,19 @@ def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18):
     if xs[0]["S0"] is not None:
         S0 = np.ascontiguousarray(np.concatenate([x["S0"].double().numpy() for x in xs], axis=1))
     threads = min(os.cpu_count() or 1, heads)
-    t0 = time.perf_counter()
-    oracle.prefill_f64(q, k, v, la, beta, S0, nthreads=threads)
-    dt = time.perf_counter() - t0
+    # repeat the sample until about min_seconds of CPU time have been spent
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill_f64(q, k, v, la, beta, S0, nthreads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     # token-heads per second over the sample, as tokens/s of the full workload
-    tps = heads * T / dt / cfg.H
+    tps = passes * heads * T / dt / cfg.H
     return dict(value=tps, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{heads} of {cfg.H} heads x first {T} of {cfg.T} tokens (B=1), "
-                       f"fp64 token loop, {dt:.2f} s on {threads} threads; "
+                       f"fp64 token loop, {passes} passes in {dt:.1f} s on {threads} threads; "
                        f"rate scaled to {cfg.H} heads")
 
 

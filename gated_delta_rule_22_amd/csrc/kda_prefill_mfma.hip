@@ -53,7 +53,7 @@ constexpr int DK = 128;
 constexpr int C = 64;
 constexpr int KS = 136;            // padded row stride (bf16) of [64][128] tiles
 constexpr int TS = 72;             // padded row stride (bf16) of [*][64] tiles
-constexpr int LDT = 16 * 16 + 4;   // fp32 stride of one transposed diagonal L block
+constexpr int LDT = 16 * 16 + 4;   // fp32 stride of one diagonal L block
 // A chunk whose token ranges all decay by at most exp(-kRangeDecay) per
 // channel uses the chunk-level decay reference (1/a <= exp(8 * kRangeDecay)).
 constexpr float kRangeDecay = 8.f;
@@ -74,7 +74,7 @@ struct Prep {
     bf16x8 Mop[6][64];   // M_qk as A operands (0,0),(1,0),(2,0),(3,0),(2,1),(3,1)
     bf16x4 NLt[6][64];   // -L_IJ, J < I, as 16x16x16 A operands, pair I(I-1)/2 + J
     bf16x4 Dt[4][64];    // (I + L_II)^{-1} as 16x16x16 A operands
-    float Lt[4 * LDT];   // diagonal blocks of L, fp32, [s][t]
+    float Lt[4 * LDT];   // diagonal blocks of L, fp32, row-major [t][s]
     float P[4 * DK];     // decay from the chunk start to the start of block I
     float G[6 * DK];     // decay over blocks J..I-1 for the 6 pairs J < I
     float alast[DK];     // decay over the whole chunk
@@ -371,19 +371,26 @@ __device__ __forceinline__ void stage2(Prep& sm, bool fast) {
         if (!diag) {
             sm.NLt[I * (I - 1) / 2 + J][lane] = __builtin_convertvector(-lv, bf16x4);
         } else {
-            float* Lt = sm.Lt + I * LDT;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Lt[(4 * g + i) * 16 + r] = lv[i];   // [s][t]
+            float* Lr = sm.Lt + I * LDT;
+            *reinterpret_cast<f32x4*>(&Lr[r * 16 + 4 * g]) = lv;          // row-major [t][s]
             lds_fence_wave();
-            // row r of (I + L)^{-1}: y (I + L) = e_r, backward over columns j,
-            // y_j = [j == r] - sum_{i > j} y_i L[i][j]  (zero for j > r)
-            float y[16];
+            // row r of (I + L)^{-1}: y (I + L) = e_r. Right-looking over the
+            // rows i = 15..0 of L: y_i = [i == r] + p_i, then p_j -= y_i L[i][j]
+            // for j < i, so each step is one dependent add plus independent
+            // updates (y is zero above r).
+            float y[16], p[16];
 #pragma unroll
-            for (int j = 15; j >= 0; --j) {
-                float acc = (j == r) ? 1.f : 0.f;
+            for (int j = 0; j < 16; ++j) p[j] = 0.f;
 #pragma unroll
-                for (int i = j + 1; i < 16; ++i) acc -= y[i] * Lt[j * 16 + i];
-                y[j] = acc;
+            for (int i = 15; i >= 0; --i) {
+                y[i] = ((i == r) ? 1.f : 0.f) + p[i];
+#pragma unroll
+                for (int j4 = 0; j4 < i; j4 += 4) {
+                    const f32x4 l = *reinterpret_cast<const f32x4*>(&Lr[i * 16 + j4]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (j4 + u < i) p[j4 + u] -= y[i] * l[u];
+                }
             }
             f32x4 d;
 #pragma unroll

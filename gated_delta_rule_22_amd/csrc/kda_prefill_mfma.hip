@@ -377,20 +377,25 @@ __device__ __forceinline__ void stage2(Prep& sm, bool fast) {
             // row r of (I + L)^{-1}: y (I + L) = e_r. Right-looking over the
             // rows i = 15..0 of L: y_i = [i == r] + p_i, then p_j -= y_i L[i][j]
             // for j < i, so each step is one dependent add plus independent
-            // updates (y is zero above r).
+            // updates (y is zero above r). Rows of L are read two steps ahead
+            // so their LDS latency overlaps the updates.
             float y[16], p[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) p[j] = 0.f;
+            f32x4 row[3][4];
+            auto load_row = [&](f32x4 (&dst)[4], int i) {
+#pragma unroll
+                for (int j4 = 0; j4 < 16; j4 += 4)
+                    if (j4 < i) dst[j4 / 4] = *reinterpret_cast<const f32x4*>(&Lr[i * 16 + j4]);
+            };
+            load_row(row[15 % 3], 15);
+            load_row(row[14 % 3], 14);
 #pragma unroll
             for (int i = 15; i >= 0; --i) {
+                if (i >= 2) load_row(row[(i - 2) % 3], i - 2);
                 y[i] = ((i == r) ? 1.f : 0.f) + p[i];
 #pragma unroll
-                for (int j4 = 0; j4 < i; j4 += 4) {
-                    const f32x4 l = *reinterpret_cast<const f32x4*>(&Lr[i * 16 + j4]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (j4 + u < i) p[j4 + u] -= y[i] * l[u];
-                }
+                for (int j = 0; j < i; ++j) p[j] -= y[i] * row[i % 3][j / 4][j % 4];
             }
             f32x4 d;
 #pragma unroll

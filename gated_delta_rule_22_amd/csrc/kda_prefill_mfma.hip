@@ -743,14 +743,15 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
 // fetches in the phase where it is off the chain (one 1 KB load takes a wave
 // tens of cycles to issue): the S waves and output tiles 0, 1 in phase 1,
 // the U waves and output tiles 2, 3 in phase 2. The column tiles of a head
-// run on one XCD (block ids sharing id % 8) and share its L2. The U and S
-// waves run at raised priority so the output waves sharing their SIMDs do
-// not delay the chain.
+// run on one XCD (block ids sharing id % 8) and share its L2; when the
+// workspace streams from HBM a thirteenth wave prefetches records into that
+// L2 ahead of the role waves. The U and S waves run at raised priority so the
+// output waves sharing their SIMDs do not delay the chain.
 namespace mf {
 constexpr int PF = 4;   // operand sets in flight per wave
 }
 
-__global__ __launch_bounds__(768, 1) void prefill_state_kernel(
+__global__ __launch_bounds__(832, 1) void prefill_state_kernel(
     const char* __restrict__ ws, const float* S0, bf16* __restrict__ o, float* S_final,
     int T, int H, int BH)
 {
@@ -850,9 +851,9 @@ __global__ __launch_bounds__(768, 1) void prefill_state_kernel(
         sSB[s][lane] = pack8(Sacc[0], Sacc[1]);
         walk(sets, [&](Ops& x, Ops& px, int c, auto) {
             lds_barrier();                                   // S_c ready
+            load(px, c + PF - 1);
             Sacc[0] *= x.al[0];
             Sacc[1] *= x.al[1];
-            load(px, c + PF - 1);
             lds_barrier();                                   // U_c ready
             const bf16x8 UB0 = *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]);
             const bf16x8 UB1 = *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]);
@@ -870,6 +871,38 @@ __global__ __launch_bounds__(768, 1) void prefill_state_kernel(
                 for (int i = 0; i < 4; ++i)
                     S_final[sbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol] = Sacc[m][i];
         }
+    } else if (wave == 12) {
+        // ---- L2 prefetch (launched only for workspaces that stream from HBM):
+        //      this workgroup's eighth of the record eight chunks ahead, one
+        //      dword per 128-byte line, so that the role waves of the head's
+        //      eight column tiles (one XCD, one L2) hit L2 ----
+        constexpr int kAhead = PF + 2;
+        constexpr int kSlice = REC_BYTES / 8;
+        uint32_t ring[3][2] = {};
+        uint32_t acc = 0;
+        auto touch = [&](uint32_t (&dst)[2], int c) {
+            const char* rp = rec(c);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int off = min(ct * kSlice + (u * 64 + lane) * 128, REC_BYTES - 4);
+                dst[u] = *reinterpret_cast<const uint32_t*>(rp + off);
+            }
+        };
+        touch(ring[0], kAhead);
+        touch(ring[1], kAhead + 1);
+        for (int c = 0; c < nchunks; c += 3) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (c + k < nchunks) {
+                    lds_barrier();                           // S_c ready
+                    acc ^= ring[(k + 2) % 3][0] ^ ring[(k + 2) % 3][1];   // oldest set: long arrived
+                    touch(ring[(k + 2) % 3], c + k + kAhead + 2);
+                    lds_barrier();                           // U_c ready
+                }
+            }
+        }
+        // keep the fetches alive; never true for a real call
+        if (acc == 0x9e3779b9u && T < 0) o[lane] = (bf16)(float)acc;
     } else {
         // ---- O = Q_decay S + M_qk U, token tile I ----
         const int I = wave - 8;
@@ -894,17 +927,21 @@ __global__ __launch_bounds__(768, 1) void prefill_state_kernel(
             Ops sets[PF];
 #pragma unroll
             for (int k = 0; k < PF - 1; ++k) load(sets[k], k);
-            if (!kEarly) load(sets[PF - 1], PF - 1);
             walk(sets, [&](Ops& x, Ops& px, int c, auto full) {
+                // fetches go first in their phase, into the set the previous
+                // chunk freed, so they drain while this wave computes
                 lds_barrier();                               // S_c ready
-                f32x4 O = zero4();
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) O = mma32(x.q[kk], sSB[kk][lane], O);
                 if (kEarly) load(px, c + PF - 1);
+                f32x4 Oa = zero4(), Ob = zero4();
+                Oa = mma32(x.q[0], sSB[0][lane], Oa);
+                Ob = mma32(x.q[1], sSB[1][lane], Ob);
+                Oa = mma32(x.q[2], sSB[2][lane], Oa);
+                Ob = mma32(x.q[3], sSB[3][lane], Ob);
                 lds_barrier();                               // U_c ready
-                O = mma32(x.m0, *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]), O);
-                if (I >= 2) O = mma32(x.m1, *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]), O);
-                if (!kEarly) load(x, c + PF);
+                if (!kEarly) load(px, c + PF - 1);
+                f32x4 O = mma32(x.m0, *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]), Oa);
+                if (I >= 2) Ob = mma32(x.m1, *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]), Ob);
+                O += Ob;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tile[(4 * g + e) * 16 + r] = (bf16)O[e];
                 lds_fence_wave();
@@ -969,7 +1006,11 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long groups = (heads + 7) / 8;   // 8 heads x 8 column tiles per group of 64 blocks
-    hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)(groups * 64)), dim3(768), 0, st,
+    // A workspace that outgrows the last-level cache (256 MB) streams from
+    // HBM: add the L2 prefetch wave (thirteenth wave) for it.
+    const size_t ws_bytes = (size_t)heads * nchunks * mf::REC_BYTES;
+    const unsigned threads = ws_bytes > (size_t(128) << 20) ? 832u : 768u;
+    hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)(groups * 64)), dim3(threads), 0, st,
                        (const char*)ws, S0, (bf16*)o, S_final, T, H, (int)heads);
     return hipGetLastError();
 }

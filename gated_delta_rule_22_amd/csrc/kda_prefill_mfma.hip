@@ -632,9 +632,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         const bool fast = chunk_is_mild<NW>(sm);
         if (ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
         else stage1b<NW, false>(sm, in, ntok, fast);
-        if (c + 1 < nchunks) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
+        // next chunk's inputs; with 8 waves, waves 4-7 (lighter Gram work)
+        // fetch after stage 2, so their fetches queue while the inverses finish
+        const bool early_fetch = NW < 8 || wave < 4;
+        if (c + 1 < nchunks && early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
         lds_barrier();
         stage2<NW>(sm, fast);
+        if (c + 1 < nchunks && !early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
@@ -684,9 +688,12 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         const bool fast = chunk_is_mild<NW>(sm);
         if (ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
         else stage1b<NW, false>(sm, in, ntok, fast);
-        if (c + 1 < c1) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
+        // next chunk's inputs: waves 0-3 now; waves 4-7 (lighter Gram work)
+        // after stage 2, so their fetches queue while the inverses finish
+        if (c + 1 < c1 && wave < 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
         lds_barrier();
         stage2<NW>(sm, fast);
+        if (c + 1 < c1 && wave >= 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);

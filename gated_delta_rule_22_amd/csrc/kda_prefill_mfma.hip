@@ -472,8 +472,8 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
 // U = U0 - W S, O = Q_decay S + M_qk U, S = Diag(a_last) S + K_restore^T U.
 // O[I] receives rows 16I + 4g + (0..3) of column r (MFMA accumulator layout).
 // PRELOAD reads all LDS operands of a pass before its MFMAs so the reads
-// overlap (needs ~130 more registers); otherwise each operand is read where
-// it is used.
+// overlap (needs ~130 more registers); otherwise the reads run a few MFMA
+// steps ahead of their use.
 // `between(k)` is called after the k-th of four MFMA groups (k = 0..3) so a
 // caller can slot other instructions (the next chunk's loads) under the MFMAs.
 struct NoOp { __device__ void operator()(int) const {} };
@@ -519,13 +519,65 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
+        // LDS operand reads run D steps ahead of their MFMAs (step s = kk * 4
+        // + I: consecutive steps feed independent accumulators); the M_qk
+        // operands are read in the last steps, when no W/Q reads remain
+        constexpr int D = 3;
+        bf16x8 bw[D], bq[D], mop[6];
+        auto ld_wq = [&](int s, bf16x8& w, bf16x8& q) {
+            const int I = s & 3, kk = s >> 2;
+            w = nW[I * 4 + kk][lane];
+            q = ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g);
+        };
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+        for (int s = 0; s < D; ++s) ld_wq(s, bw[s], bq[s]);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                accU[I] = mma32(nW[I * 4 + kk][lane], SB[kk], accU[I]);
-                O[I] = mma32(ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g), SB[kk], O[I]);
+        for (int s = 0; s < 16; ++s) {
+            const int I = s & 3, kk = s >> 2;
+            const bf16x8 w = bw[s % D], q = bq[s % D];
+            if (s + D < 16) {
+                ld_wq(s + D, bw[s % D], bq[s % D]);
+            } else {
+                const int j = 2 * (s + D - 16);       // 0, 2, 4
+                mop[j] = M[j][lane];
+                mop[j + 1] = M[j + 1][lane];
             }
+            __builtin_amdgcn_sched_barrier(0);
+            accU[I] = mma32(w, SB[kk], accU[I]);
+            O[I] = mma32(q, SB[kk], O[I]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 UB[2];
+        UB[0] = pack8(accU[0], accU[1]);
+        UB[1] = pack8(accU[2], accU[3]);
+        // K_restore^T pairs, two ahead
+        bf16x8 bk[2][2];
+        f32x4 bal[2];
+        auto ld_k = [&](int m, bf16x8 (&kb)[2], f32x4& al) {
+            kb[0] = ldA_perm(KrT + (16 * m + r) * TS, 0, g);
+            kb[1] = ldA_perm(KrT + (16 * m + r) * TS, 32, g);
+            al = *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
+        };
+        ld_k(0, bk[0], bal[0]);
+        ld_k(1, bk[1], bal[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) O[I] = mma32(mop[I], UB[0], O[I]);
+        O[2] = mma32(mop[4], UB[1], O[2]);
+        O[3] = mma32(mop[5], UB[1], O[3]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const bf16x8 k0 = bk[m & 1][0], k1 = bk[m & 1][1];
+            const f32x4 al = bal[m & 1];
+            if (m + 2 < 8) ld_k(m + 2, bk[m & 1], bal[m & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            Sacc[m] *= al;
+            Sacc[m] = mma32(k0, UB[0], Sacc[m]);
+            Sacc[m] = mma32(k1, UB[1], Sacc[m]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
     }
     bf16x8 UB[2];
     UB[0] = pack8(accU[0], accU[1]);
@@ -535,7 +587,7 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
     for (int I = 0; I < 4; ++I) O[I] = mma32(M[I][lane], UB[0], O[I]);
     O[2] = mma32(M[4][lane], UB[1], O[2]);
     O[3] = mma32(M[5][lane], UB[1], O[3]);
-    if (PRELOAD) {
+    {
         bf16x8 aK[8][2];
         f32x4 al[8];
 #pragma unroll
@@ -550,13 +602,6 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
             Sacc[m] *= al[m];
             Sacc[m] = mma32(aK[m][0], UB[0], Sacc[m]);
             Sacc[m] = mma32(aK[m][1], UB[1], Sacc[m]);
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            Sacc[m] *= *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
-            Sacc[m] = mma32(ldA_perm(KrT + (16 * m + r) * TS, 0, g), UB[0], Sacc[m]);
-            Sacc[m] = mma32(ldA_perm(KrT + (16 * m + r) * TS, 32, g), UB[1], Sacc[m]);
         }
     }
 }

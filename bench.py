@@ -161,6 +161,48 @@ def bench_decode(cfg, loops=2):
                 flops_per_step=A.decode_step_flops(cfg.B, cfg.H, cfg.dk, cfg.dv))
 
 
+def bench_decode_multi(cfg, T=8, reps=20):
+    """An 8-token draft from the decode configuration's state: a verify pass
+    (n_commit = 0, the state is only read) and a full commit (n_commit = T)."""
+    import torch
+    import dataclasses
+    import gated_delta_rule_22_amd as kda
+    import workloads as W
+    from workloads import accounting as A
+
+    dev = torch.device("cuda:0")
+    S = W.decode_state(cfg, device=dev)
+    x = W.prefill_inputs(dataclasses.replace(W.PREFILL_CONFIGS["prefill"]), B=cfg.B, T=T,
+                         H=cfg.H, seed=cfg.seed + 77, device=dev)
+    o = torch.empty((cfg.B, T, cfg.H, cfg.dv), dtype=cfg.dtype, device=dev)
+    zeros = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    full = torch.full((cfg.B,), T, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, n in (("verify", zeros), ("commit", full)):
+        def call():
+            kda.kda_decode_multi(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S,
+                                 n_commit=n, o=o)
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+        nbytes = A.decode_multi_bytes(cfg.B, cfg.H, T, cfg.dk, cfg.dv, commit=name == "commit")
+        out[name] = {"us_per_call": us, "tokens_per_s": cfg.B * T / (us * 1e-6),
+                     "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9,
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                  "kernel": "decode_multi_kernel", "algorithmic_bytes": nbytes}}
+    out["workload"] = f"kda_decode_multi B{cfg.B} H{cfg.H} dk{cfg.dk} dv{cfg.dv} T{T} bf16"
+    return out
+
+
 def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18, min_seconds=10.0):
     """fp64 oracle on the host cores over a bounded sample of the same
     workload: whole heads (one per thread) over the first tokens of the
@@ -293,6 +335,12 @@ def main():
                          "kernel": "decode_kernel", "kernel_us": dec["kernel_us"],
                          "algorithmic_bytes": dec["bytes_per_step"]},
         }
+
+        _log("[bench] decode_multi (8-token draft: verify, commit)")
+        dm = bench_decode_multi(dc)
+        _log(f"[bench] decode_multi verify {dm['verify']['us_per_call']:.1f} us, "
+             f"commit {dm['commit']['us_per_call']:.1f} us")
+        result["decode_multi"] = dm
 
     if not args.no_cpu:
         _log("[bench] cpu oracle baseline")

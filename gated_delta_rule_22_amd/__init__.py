@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "KDAError", "lib_path", "load_library", "kda_status_string",
-    "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_decode_step",
+    "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_decode_step", "kda_decode_multi",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +57,8 @@ def load_library():
     lib.kda_prefill_fwd.restype = i
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, vp]
     lib.kda_decode_step.restype = i
+    lib.kda_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, vp]
+    lib.kda_decode_multi.restype = i
     _lib = lib
     return lib
 
@@ -159,4 +161,40 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              _ptr(o), B, H, dk, dv, _DTYPES[dt], _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_decode_step")
+    return o
+
+
+def kda_decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     log_alpha: torch.Tensor, beta: torch.Tensor, S: torch.Tensor, *,
+                     n_commit: Optional[torch.Tensor] = None,
+                     o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """T tokens per sequence from the live state S [B,H,dk,dv] (fp32): returns
+    o [B,T,H,dv] for every token and overwrites S[b] with the state after the
+    first n_commit[b] tokens (int32 [B] on the device; None = all T; 0 leaves
+    S[b] untouched)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_decode_multi needs GPU tensors")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, T, H, dk), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check(S, "S", (B, H, dk, dv), torch.float32, dev)
+    if n_commit is not None:
+        _check(n_commit, "n_commit", (B,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, T, H, dv), dt, dev)
+    st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                              _ptr(o), _ptr(n_commit), B, T, H, dk, dv, _DTYPES[dt],
+                              _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_multi")
     return o

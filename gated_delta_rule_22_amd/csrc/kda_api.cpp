@@ -141,4 +141,38 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_decode_multi(const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta,
+                            float* S, void* o, const int* n_commit,
+                            int B, int T, int H, int dk, int dv,
+                            kda_dtype dtype, void* stream) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (n_commit && ((uintptr_t)n_commit & 3u)) return KDA_ERR_INVALID_ARG;
+    const size_t elt = dtype == KDA_BF16 ? 2 : 4;
+    size_t bh = 1, tok = 1;
+    if (!mul_ok(bh, (size_t)B) || !mul_ok(bh, (size_t)H)) return KDA_ERR_INVALID_ARG;
+    if (bh > (size_t)INT32_MAX / 4) return KDA_ERR_INVALID_ARG;
+    if (!mul_ok(tok, bh) || !mul_ok(tok, (size_t)T) || tok > (SIZE_MAX >> 10))
+        return KDA_ERR_INVALID_ARG;
+    const size_t nk = tok * dk, nv = tok * dv, ns = bh * dk * dv;
+    const Range rq(q, nk * elt), rk(k, nk * elt), rv(v, nv * elt), rla(log_alpha, nk * 4),
+        rb(beta, tok * 4), rS(S, ns * 4), ro(o, nv * elt), rn(n_commit, n_commit ? (size_t)B * 4 : 0);
+    const Range ins[] = {rq, rk, rv, rla, rb, rn};
+    for (const Range& in : ins)
+        if (overlap(ro, in) || overlap(rS, in)) return KDA_ERR_INVALID_ARG;
+    if (overlap(ro, rS)) return KDA_ERR_INVALID_ARG;
+
+    const hipError_t e = kda::launch_decode_multi(dtype == KDA_BF16, dk, dv, q, k, v, log_alpha,
+                                                  beta, S, o, n_commit, (int)bh, H, T,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

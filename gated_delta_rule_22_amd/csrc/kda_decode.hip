@@ -21,10 +21,28 @@
 
 namespace kda {
 
+// N consecutive row values of one lane, with 16-byte loads where the row
+// count allows (the row offset is a multiple of N, so the vectors are aligned).
 template <typename T, int N>
 __device__ __forceinline__ void load_row_vals(const T* __restrict__ p, float (&out)[N]) {
+    if constexpr (sizeof(T) == 2 && N % 8 == 0) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = to_f32(p[i]);
+        for (int i = 0; i < N; i += 8) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + i);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) out[i + j] = (float)x[j];
+        }
+    } else if constexpr (sizeof(T) == 4 && N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p + i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[i + j] = x[j];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = to_f32(p[i]);
+    }
 }
 
 template <int DK, int DV, typename T>
@@ -60,8 +78,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     float kr[RPL], qr[RPL], lar[RPL];
     load_row_vals<T, RPL>(k + (size_t)head * DK + row0, kr);
     load_row_vals<T, RPL>(q + (size_t)head * DK + row0, qr);
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) lar[r] = log_alpha[(size_t)head * DK + row0 + r];
+    load_row_vals<float, RPL>(log_alpha + (size_t)head * DK + row0, lar);
     float vv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[(size_t)head * DV + col + c]);
@@ -105,6 +122,93 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 }
 
+// Multi-token decode from a live state: T tokens per sequence applied in
+// order with the same per-token step, the state slice staying in registers,
+// o written for every token, and the state written back once, right after
+// token n = n_commit[b] (clamped to [0, T]; none when n = 0). A verify pass
+// (n = 0) thus reads each state element once and writes none; a commit or a
+// plain multi-token step reads and writes it once.
+template <int DK, int DV, typename T>
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    float* __restrict__ S, T* __restrict__ o, const int* __restrict__ n_commit,
+    int BH, int H, int ntok)
+{
+    constexpr int NC = DV < 32 ? DV : 32;
+    constexpr int NCG = NC / 4;
+    constexpr int NRG = kWave / NCG;
+    constexpr int RPL = DK / NRG;
+    constexpr int SLICES = DV / NC;
+    static_assert(RPL >= 1 && RPL * NRG == DK, "dk must cover every row group");
+
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int head = gw / SLICES;
+    if (head >= BH) return;
+    const int slice = gw - head * SLICES;
+    const int cg = lane % NCG;
+    const int rg = lane / NCG;
+    const int col = slice * NC + cg * 4;
+    const int row0 = rg * RPL;
+    const int bb = head / H, hh = head - bb * H;
+    int n = n_commit ? n_commit[bb] : ntok;
+    n = __builtin_amdgcn_readfirstlane(min(max(n, 0), ntok));
+
+    float* Sh = S + (size_t)head * DK * DV;
+    f32x4 s[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+        s[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+
+    for (int t = 0; t < ntok; ++t) {
+        const size_t tok = ((size_t)bb * ntok + t) * H + hh;
+        float kr[RPL], qr[RPL], lar[RPL];
+        load_row_vals<T, RPL>(k + tok * DK + row0, kr);
+        load_row_vals<T, RPL>(q + tok * DK + row0, qr);
+        load_row_vals<float, RPL>(log_alpha + tok * DK + row0, lar);
+        float vv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[tok * DV + col + c]);
+        const float b = beta[tok];
+
+        f32x4 w = zero4(), p = zero4();
+        float kq = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            s[r] *= exp_e(lar[r]);
+            w += s[r] * kr[r];
+            p += s[r] * qr[r];
+            kq += kr[r] * qr[r];
+        }
+#pragma unroll
+        for (int off = NCG; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                w[c] += __shfl_xor(w[c], off);
+                p[c] += __shfl_xor(p[c], off);
+            }
+            kq += __shfl_xor(kq, off);
+        }
+        f32x4 u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u[c] = b * (vv[c] - w[c]);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) s[r] += kr[r] * u;
+        if (rg == 0) {
+            T* ot = o + tok * DV + col;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ot[c] = from_f32<T>(p[c] + u[c] * kq);
+        }
+        if (t + 1 == n) {
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+                __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+        }
+    }
+}
+
 template <int DK, int DV, typename T>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* la,
                                   const float* beta, float* S, void* o, int BH, hipStream_t st)
@@ -131,6 +235,46 @@ static hipError_t dispatch_dv(int dk, int dv, const void* q, const void* k, cons
     KDA_DEC_CASE(128, 16) KDA_DEC_CASE(128, 32) KDA_DEC_CASE(128, 64) KDA_DEC_CASE(128, 128)
 #undef KDA_DEC_CASE
     return hipErrorInvalidValue;
+}
+
+template <int DK, int DV, typename T>
+static hipError_t launch_decode_multi_t(const void* q, const void* k, const void* v,
+                                        const float* la, const float* beta, float* S, void* o,
+                                        const int* n_commit, int BH, int H, int ntok,
+                                        hipStream_t st)
+{
+    constexpr int NC = DV < 32 ? DV : 32;
+    const long waves = (long)BH * (DV / NC);
+    const long blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, T>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const T*)q, (const T*)k, (const T*)v, la, beta, S, (T*)o, n_commit, BH,
+                       H, ntok);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_multi(int dk, int dv, const void* q, const void* k, const void* v,
+                                 const float* la, const float* beta, float* S, void* o,
+                                 const int* n_commit, int BH, int H, int ntok, hipStream_t st)
+{
+#define KDA_DEC_CASE(DKV, DVV) \
+    if (dk == DKV && dv == DVV) \
+        return launch_decode_multi_t<DKV, DVV, T>(q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
+    KDA_DEC_CASE(16, 16) KDA_DEC_CASE(16, 32) KDA_DEC_CASE(16, 64) KDA_DEC_CASE(16, 128)
+    KDA_DEC_CASE(32, 16) KDA_DEC_CASE(32, 32) KDA_DEC_CASE(32, 64) KDA_DEC_CASE(32, 128)
+    KDA_DEC_CASE(64, 16) KDA_DEC_CASE(64, 32) KDA_DEC_CASE(64, 64) KDA_DEC_CASE(64, 128)
+    KDA_DEC_CASE(128, 16) KDA_DEC_CASE(128, 32) KDA_DEC_CASE(128, 64) KDA_DEC_CASE(128, 128)
+#undef KDA_DEC_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, const void* k,
+                               const void* v, const float* la, const float* beta, float* S,
+                               void* o, const int* n_commit, int BH, int H, int ntok,
+                               hipStream_t st)
+{
+    if (bf16_io) return dispatch_multi<bf16>(dk, dv, q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
+    return dispatch_multi<float>(dk, dv, q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
 }
 
 hipError_t launch_decode(bool bf16_io, int dk, int dv, const void* q, const void* k,

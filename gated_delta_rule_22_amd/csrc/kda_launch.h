@@ -11,6 +11,13 @@ hipError_t launch_decode(bool bf16_io, int dk, int dv, const void* q, const void
                          const void* v, const float* la, const float* beta, float* S,
                          void* o, int BH, hipStream_t st);
 
+// Multi-token decode over B*H heads, T = ntok tokens each; S advanced by the
+// first n_commit[b] tokens (all when n_commit is null).
+hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, const void* k,
+                               const void* v, const float* la, const float* beta, float* S,
+                               void* o, const int* n_commit, int BH, int H, int ntok,
+                               hipStream_t st);
+
 // Generic chunked prefill (fp32 arithmetic, any supported dk/dv/chunk, fp32 or bf16 I/O).
 hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, const void* v,
                                   const float* la, const float* beta, const float* S0,

@@ -102,6 +102,31 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            int B, int H, int dk, int dv,
                            kda_dtype dtype, void* stream);
 
+/*
+ * Multi-token decode from a live state, for verifying a drafted continuation
+ * (the trillion-scale architecture page, section 6: a one-layer draft
+ * proposes up to seven tokens that the model checks in one pass) and for
+ * short multi-token steps. For each sequence b the recurrence runs over its
+ * T tokens in order from S[b]:
+ *   q, k, log_alpha [B,T,H,dk]; v, o [B,T,H,dv]; beta [B,T,H]; S [B,H,dk,dv]
+ *   o         o_t for every token t, read from the state after token t of the
+ *             T-token run (as in prefill)
+ *   n_commit  device int32 [B] (4-byte aligned) or NULL: S[b] is overwritten
+ *             with the state after its first n_commit[b] tokens, the accepted
+ *             prefix; values are clamped to [0, T]; NULL means T. With 0, S[b]
+ *             is left untouched (a verify pass), so a rejected draft needs no
+ *             rollback copy.
+ * Each state element is read once and written at most once. o must not
+ * overlap an input, S or n_commit; S must not overlap an input. T = 0 is a
+ * no-op. T is meant to be small (a draft); long sequences belong to
+ * kda_prefill_fwd.
+ */
+kda_status kda_decode_multi(const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta,
+                            float* S, void* o, const int* n_commit,
+                            int B, int T, int H, int dk, int dv,
+                            kda_dtype dtype, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* kda_status_string(kda_status status);
 

@@ -31,7 +31,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert set(syms) == {"kda_prefill_workspace_size", "kda_prefill_fwd",
-                         "kda_decode_step", "kda_status_string"}
+                         "kda_decode_step", "kda_decode_multi", "kda_status_string"}
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -116,6 +116,26 @@ def test_decode_rejects(lib):
     assert decode(lib, o=P(5, 512)) == INVALID       # o inside S
     assert decode(lib, S=P(1, 64)) == INVALID        # S overlapping k
     assert decode(lib, B=0) == OK
+
+
+def multi(lib, *, q=P(0), k=P(1), v=P(2), la=P(3), beta=P(4), S=P(5), o=P(6), n=P(7),
+          B=2, T=4, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_decode_multi(q, k, v, la, beta, S, o, n, B, T, H, dk, dv, dt, None)
+
+
+def test_decode_multi_rejects(lib):
+    assert multi(lib, T=-1) == INVALID
+    assert multi(lib, dv=48) == UNSUPPORTED
+    assert multi(lib, dt=2) == UNSUPPORTED
+    for name in ("q", "k", "v", "la", "beta", "S", "o"):
+        assert multi(lib, **{name: None}) == INVALID, name
+        assert multi(lib, **{name: P(9, 8)}) == INVALID, name
+    assert multi(lib, n=P(7, 2)) == INVALID          # n_commit not 4-byte aligned
+    assert multi(lib, o=P(7, 0)) == INVALID          # o overlapping n_commit
+    assert multi(lib, S=P(0, 256)) == INVALID        # S overlapping q
+    assert multi(lib, o=P(5, 64)) == INVALID         # o inside S
+    assert multi(lib, T=0) == OK                     # nothing to do
+    assert multi(lib, B=0) == OK
 
 
 def test_binding_rejects_cpu_tensors():

@@ -54,6 +54,15 @@ def decode_step_bytes(B: int, H: int, dk: int, dv: int, elt: int = 2) -> int:
     return B * H * (8 * dk * dv + elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv)
 
 
+def decode_multi_bytes(B: int, H: int, T: int, dk: int, dv: int, commit: bool,
+                       elt: int = 2) -> int:
+    """Multi-token decode: the fp32 state read once (and written once when a
+    prefix is committed) plus T tokens of q, k, v, o, log-decay and beta."""
+    state = 4 * dk * dv * (2 if commit else 1)
+    per_token = elt * (2 * dk + dv) + 4 * dk + 4 + elt * dv
+    return B * H * (state + T * per_token)
+
+
 def decode_step_flops(B: int, H: int, dk: int, dv: int) -> int:
     return 7 * dk * dv * B * H
 

@@ -6,6 +6,9 @@ and this package imports nothing from the product package.
 
 ``prefill_f64`` / ``decode_f64`` wrap the plain C token-by-token recurrence in
 ``kda_oracle.c`` (definition: Kimi K3 blog, section "Kimi Delta Attention").
+``prefill_varlen_f64`` runs the same recurrence over packed sequences and
+records the state at fixed token intervals (the checkpoints a prefix cache
+keeps: "Kimi K3: the manos...", section "KDA Prefix Cache Management").
 ``chunk_form`` holds an independent fp64 NumPy statement of the chunked
 unrolling (FlashKDA algorithm, "Kimi K3: the manos..." section "FlashKDA
 Algorithm"), used by tests only to pin the chunk algebra against the step form.
@@ -90,6 +93,43 @@ def prefill_f64(q, k, v, log_alpha, beta, S0=None, nthreads=None, want_o=True):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return o, S
+
+
+def prefill_varlen_f64(q, k, v, log_alpha, beta, cu_seqlens, S0=None, ckpt_every=0,
+                       nthreads=None):
+    """Packed sequences: q, k, log_alpha [T,H,dk]; v [T,H,dv]; beta [T,H];
+    sequence i is tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1 (offsets must be
+    non-decreasing inside [0, T]) and starts from S0[i] (zeros if S0 is None).
+    With ckpt_every > 0 the state after every ckpt_every tokens of each
+    sequence is recorded, sequence by sequence in order.
+    Returns (o [T,H,dv], S_final [N,H,dk,dv], S_ckpt [n_ckpt,H,dk,dv])."""
+    q, k, v, la, beta, S0 = map(_f64, (q, k, v, log_alpha, beta, S0))
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = len(cu) - 1
+    if cu[0] < 0 or cu[-1] > T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing inside [0, T]")
+    o = np.zeros((T, H, dv), np.float64)
+    S_final = np.zeros((N, H, dk, dv), np.float64)
+    ckpts = []
+    for i in range(N):
+        S = np.zeros((1, H, dk, dv)) if S0 is None else S0[i:i + 1].copy()
+        a, b = cu[i], cu[i + 1]
+        # cut at every checkpoint; the token loop carries S exactly across cuts
+        cuts = list(range(a, b, ckpt_every)) + [b] if ckpt_every > 0 else [a, b]
+        for s0, s1 in zip(cuts, cuts[1:]):
+            if s1 == s0:
+                continue
+            seg = slice(s0, s1)
+            oi, S = prefill_f64(q[None, seg], k[None, seg], v[None, seg], la[None, seg],
+                                beta[None, seg], S, nthreads=nthreads)
+            o[seg] = oi[0]
+            if ckpt_every > 0 and (s1 - a) % ckpt_every == 0:
+                ckpts.append(S[0].copy())
+        S_final[i] = S[0]
+    S_ckpt = np.stack(ckpts) if ckpts else np.zeros((0, H, dk, dv), np.float64)
+    return o, S_final, S_ckpt
 
 
 def decode_f64(q, k, v, log_alpha, beta, S, nthreads=None):

@@ -254,3 +254,100 @@ def test_rel_l2():
     x = np.array([3.0, 4.0])
     assert oracle.rel_l2(x, x) == 0.0
     assert abs(oracle.rel_l2(np.array([3.0, 4.0 + 0.5]), x) - 0.1) < 1e-15
+
+
+# ---- packed sequences and state checkpoints ("Kimi K3: the manos...",
+#      section "KDA Prefix Cache Management": states kept at fixed intervals)
+
+def packed_inputs(lengths, H, dk, dv, seed, la_hi=0.2):
+    T = sum(lengths)
+    q, k, v, la, beta, _ = rand_inputs(1, T, H, dk, dv, seed, la_hi=la_hi, s0=False)
+    S0 = 0.3 * np.random.default_rng(seed + 1).standard_normal((len(lengths), H, dk, dv))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(int).tolist()
+    return q[0], k[0], v[0], la[0], beta[0], S0, cu
+
+
+def test_varlen_orthonormal_keys_closed_form():
+    # alpha = 1, beta = 1, S0 = 0, orthonormal keys inside each sequence:
+    # the state after j tokens of a sequence is sum_{t<j} k_t v_t^T (each write
+    # leaves the earlier, orthogonal keys alone), and o_t = S_t^T q_t.
+    rng = np.random.default_rng(30)
+    d, dv, K = 12, 5, 3
+    lengths = [7, 0, 12, 4]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(int)
+    k = np.zeros((T, 1, d))
+    for a, b in zip(cu, cu[1:]):
+        Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+        k[a:b, 0] = Qm.T[: b - a]
+    q = rng.standard_normal((T, 1, d))
+    v = rng.standard_normal((T, 1, dv))
+    o, S, Sc = oracle.prefill_varlen_f64(q, k, v, np.zeros((T, 1, d)), np.ones((T, 1)),
+                                         cu.tolist(), None, ckpt_every=K)
+    ck = []
+    for i, (a, b) in enumerate(zip(cu, cu[1:])):
+        run = np.zeros((d, dv))
+        for t in range(a, b):
+            run = run + np.outer(k[t, 0], v[t, 0])
+            np.testing.assert_allclose(o[t, 0], run.T @ q[t, 0], atol=1e-12)
+            if (t + 1 - a) % K == 0:
+                ck.append(run)
+        np.testing.assert_allclose(S[i, 0], run, atol=1e-12)
+    assert Sc.shape[0] == sum(n // K for n in lengths) == len(ck)
+    np.testing.assert_allclose(Sc[:, 0], np.stack(ck), atol=1e-12)
+
+
+def test_varlen_pure_decay_closed_form():
+    # beta = 0: no writes, S_t = Diag(exp(sum of log-decays)) S0[i] per
+    # sequence; checkpoints at every K tokens of the sequence.
+    lengths, K = [5, 9, 0, 4], 2
+    q, k, v, la, beta, S0, cu = packed_inputs(lengths, 2, 6, 3, 31, la_hi=1.0)
+    beta[:] = 0.0
+    o, S, Sc = oracle.prefill_varlen_f64(q, k, v, la, beta, cu, S0, ckpt_every=K)
+    ck = []
+    for i, (a, b) in enumerate(zip(cu, cu[1:])):
+        for t in range(a, b):
+            St = np.exp(la[a:t + 1].sum(0))[:, :, None] * S0[i]
+            np.testing.assert_allclose(o[t], np.einsum("hkv,hk->hv", St, q[t]), atol=1e-13)
+            if (t + 1 - a) % K == 0:
+                ck.append(St)
+        Sb = np.exp(la[a:b].sum(0))[:, :, None] * S0[i]
+        np.testing.assert_allclose(S[i], Sb, atol=1e-13)
+    np.testing.assert_allclose(Sc, np.stack(ck), atol=1e-13)
+
+
+def test_varlen_equals_independent_chunk_form():
+    # every sequence against the independent NumPy chunk statement from its
+    # own S0; checkpoint j = that statement's state after j*K tokens
+    lengths, K = [11, 1, 0, 20], 4
+    q, k, v, la, beta, S0, cu = packed_inputs(lengths, 2, 8, 5, 32)
+    o, S, Sc = oracle.prefill_varlen_f64(q, k, v, la, beta, cu, S0, ckpt_every=K)
+    slot = 0
+    for i, (a, b) in enumerate(zip(cu, cu[1:])):
+        sl = lambda x, n=b: x[None, a:n]
+        oc, Scf = chunked_prefill_f64(sl(q), sl(k), sl(v), sl(la), sl(beta), S0[i:i + 1], 8)
+        np.testing.assert_allclose(o[a:b], oc[0], atol=1e-12)
+        np.testing.assert_allclose(S[i], Scf[0], atol=1e-12)
+        for j in range(1, (b - a) // K + 1):
+            n = a + j * K
+            _, Sj = chunked_prefill_f64(sl(q, n), sl(k, n), sl(v, n), sl(la, n), sl(beta, n),
+                                        S0[i:i + 1], 8)
+            np.testing.assert_allclose(Sc[slot], Sj[0], atol=1e-12)
+            slot += 1
+    assert slot == Sc.shape[0]
+
+
+def test_varlen_sequences_are_independent():
+    # changing one sequence's tokens and initial state changes nothing else
+    lengths = [6, 9, 5]
+    q, k, v, la, beta, S0, cu = packed_inputs(lengths, 2, 4, 4, 33)
+    o1, S1, C1 = oracle.prefill_varlen_f64(q, k, v, la, beta, cu, S0, ckpt_every=3)
+    v2, S02 = v.copy(), S0.copy()
+    v2[6:15] += 1.0
+    S02[1] *= -2.0
+    o2, S2, C2 = oracle.prefill_varlen_f64(q, k, v2, la, beta, cu, S02, ckpt_every=3)
+    np.testing.assert_array_equal(o1[:6], o2[:6])
+    np.testing.assert_array_equal(o1[15:], o2[15:])
+    np.testing.assert_array_equal(S1[[0, 2]], S2[[0, 2]])
+    np.testing.assert_array_equal(C1[[0, 1, 5]], C2[[0, 1, 5]])   # slots of sequences 0 and 2
+    assert not np.allclose(o1[6:15], o2[6:15])

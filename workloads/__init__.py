@@ -31,6 +31,7 @@ import torch
 __all__ = [
     "PrefillConfig", "DecodeConfig", "PREFILL_CONFIGS", "DECODE_CONFIGS",
     "prefill_inputs", "prefill_inputs_per_head", "decode_state", "decode_step_inputs",
+    "VarlenConfig", "VARLEN_CONFIGS", "varlen_lengths", "varlen_inputs",
 ]
 
 
@@ -175,3 +176,68 @@ def decode_step_inputs(cfg: DecodeConfig, step: int, *, B: Optional[int] = None,
     la = _log_alpha((B, H, dk), "uniform", cfg.la_lo, cfg.la_hi, g, device)
     beta = _beta((B, H), "sigmoid", g, device)
     return dict(q=q, k=k, v=v, log_alpha=la, beta=beta)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenConfig:
+    """A packed batch of prompts of mixed lengths (serving prefill): lengths
+    log-uniform in [len_lo, len_hi] until `total` tokens, state checkpoints
+    every `ckpt_every` tokens of each prompt (the 512-token prefix-cache grid
+    on the trillion-scale architecture page, section 6). Per-token
+    distributions come from the prefill config `base`."""
+    name: str
+    total: int
+    H: int
+    len_lo: int
+    len_hi: int
+    ckpt_every: int
+    base: str
+    seed: int
+
+    def describe(self) -> str:
+        return (f"kda_prefill_varlen T{self.total} H{self.H} lengths {self.len_lo}.."
+                f"{self.len_hi} ckpt {self.ckpt_every} bf16")
+
+
+VARLEN_CONFIGS = {
+    # The batched configuration's 65,536 tokens per 32 heads, as a mix of
+    # prompt lengths instead of eight equal sequences.
+    "varlen": VarlenConfig("varlen", 65536, 32, 256, 16384, 512, "batched", 11),
+}
+
+
+def varlen_lengths(total: int, lo: int, hi: int, seed: int) -> list:
+    """Sequence lengths, log-uniform in [lo, hi], summing to exactly `total`
+    (the last one is cut to fit)."""
+    g = _gen(seed, "cpu")
+    out, acc = [], 0
+    while acc < total:
+        u = float(torch.rand((), generator=g))
+        n = int(round(lo * (hi / lo) ** u))
+        n = min(max(n, 1), total - acc)
+        out.append(n)
+        acc += n
+    return out
+
+
+def varlen_inputs(base: PrefillConfig, lengths, *, H: Optional[int] = None,
+                  seed: Optional[int] = None, device="cpu",
+                  dtype: Optional[torch.dtype] = None) -> dict:
+    """Packed inputs for sequences of the given lengths: q, k, log_alpha
+    [T, H, dk], v [T, H, dv], beta [T, H], S0 [N, H, dk, dv] (or None), and
+    cu_seqlens int32 [N + 1] on the CPU."""
+    T = int(sum(lengths))
+    N = len(lengths)
+    x = prefill_inputs(base, B=1, T=T, H=H, seed=seed, device=device, dtype=dtype)
+    out = {n: x[n][0] for n in ("q", "k", "v", "log_alpha", "beta")}
+    H_ = out["q"].shape[1]
+    S0 = None
+    if base.s0_std > 0:
+        g = _gen((base.seed if seed is None else seed) + 7_000_000, device)
+        S0 = base.s0_std * torch.randn((N, H_, base.dk, base.dv), generator=g, device=device)
+    out["S0"] = S0
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32)
+    return out

@@ -203,6 +203,56 @@ def bench_decode_multi(cfg, T=8, reps=20):
     return out
 
 
+def bench_varlen(vc, reps=5):
+    """The packed serving-style batch (mixed prompt lengths, one kda_prefill_varlen
+    call) with and without state checkpoints."""
+    import torch
+    import gated_delta_rule_22_amd as kda
+    import workloads as W
+    from workloads import accounting as A
+
+    dev = torch.device("cuda:0")
+    base = W.PREFILL_CONFIGS[vc.base]
+    lengths = W.varlen_lengths(vc.total, vc.len_lo, vc.len_hi, vc.seed)
+    x = W.varlen_inputs(base, lengths, H=vc.H, seed=vc.seed, device=dev)
+    cu = x["cu_seqlens"].to(dev)
+    N, T, H = len(lengths), vc.total, vc.H
+    o = torch.empty_like(x["v"])
+    Sf = torch.empty((N, H, base.dk, base.dv), dtype=torch.float32, device=dev)
+    n_ck = sum(n // vc.ckpt_every for n in lengths)
+    Sc = torch.empty((max(n_ck, 1), H, base.dk, base.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.kda_prefill_varlen_workspace_size(N, T, H, base.dk, base.dv,
+                                                           base.dtype), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"workload": vc.describe(), "sequences": N, "longest": max(lengths)}
+    for name, every in (("ckpt", vc.ckpt_every), ("no_ckpt", 0)):
+        def call():
+            kda.kda_prefill_varlen(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], cu,
+                                   x["S0"], ckpt_every=every, o=o, S_final=Sf,
+                                   S_ckpt=Sc if every else None, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+        nbytes = A.prefill_bytes(1, T, H, base.dk, base.dv, elt=2, has_s0=True,
+                                 writes_state=False) + N * H * 4 * base.dk * base.dv
+        if every:
+            nbytes += n_ck * H * 4 * base.dk * base.dv
+        out[name] = {"us_per_call": us, "tokens_per_s": T / (us * 1e-6), "checkpoints": n_ck if every else 0,
+                     "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9,
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                  "algorithmic_bytes": nbytes}}
+    return out
+
+
 def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18, min_seconds=10.0):
     """fp64 oracle on the host cores over a bounded sample of the same
     workload: whole heads (one per thread) over the first tokens of the
@@ -244,6 +294,7 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["prefill", "batched", "long"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a known traffic)")
@@ -341,6 +392,14 @@ def main():
         _log(f"[bench] decode_multi verify {dm['verify']['us_per_call']:.1f} us, "
              f"commit {dm['commit']['us_per_call']:.1f} us")
         result["decode_multi"] = dm
+
+    if not args.no_varlen:
+        vc = W.VARLEN_CONFIGS["varlen"]
+        _log(f"[bench] varlen {vc.describe()}")
+        vl = bench_varlen(vc)
+        _log(f"[bench] varlen {vl['ckpt']['us_per_call']:.1f} us with checkpoints, "
+             f"{vl['no_ckpt']['us_per_call']:.1f} us without")
+        result["varlen"] = vl
 
     if not args.no_cpu:
         _log("[bench] cpu oracle baseline")

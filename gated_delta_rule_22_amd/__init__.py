@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "KDAError", "lib_path", "load_library", "kda_status_string",
-    "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_decode_step", "kda_decode_multi",
+    "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_prefill_varlen_workspace_size",
+    "kda_prefill_varlen", "kda_decode_step", "kda_decode_multi",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,11 @@ def load_library():
     lib.kda_prefill_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
                                     vp, sz, vp]
     lib.kda_prefill_fwd.restype = i
+    lib.kda_prefill_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_prefill_varlen_workspace_size.restype = sz
+    lib.kda_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, i, i,
+                                       fp, i, i, vp, sz, vp]
+    lib.kda_prefill_varlen.restype = i
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, vp]
     lib.kda_decode_step.restype = i
     lib.kda_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, vp]
@@ -133,6 +139,73 @@ def kda_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != 0:
         raise KDAError(st, "kda_prefill_fwd")
     return o, S_final
+
+
+def kda_prefill_varlen_workspace_size(N: int, T_total: int, H: int, dk: int, dv: int,
+                                      dtype: torch.dtype, chunk: int = 64) -> int:
+    return int(load_library().kda_prefill_varlen_workspace_size(N, T_total, H, dk, dv,
+                                                                _DTYPES[dtype], chunk))
+
+
+def kda_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       log_alpha: torch.Tensor, beta: torch.Tensor, cu_seqlens: torch.Tensor,
+                       S0: Optional[torch.Tensor] = None, *, ckpt_every: int = 0,
+                       ckpt_slots: Optional[int] = None, chunk: int = 64,
+                       o: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                       S_ckpt: Optional[torch.Tensor] = None, want_state: bool = True,
+                       workspace: Optional[torch.Tensor] = None, stream=None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Packed variable-length prefill. q,k,log_alpha [T,H,dk]; v [T,H,dv]; beta [T,H];
+    cu_seqlens int32 [N+1] on the device; S0 [N,H,dk,dv] fp32 or None. With
+    ckpt_every > 0 (a multiple of 64) the state after every ckpt_every tokens
+    of each sequence goes to S_ckpt [ckpt_slots,H,dk,dv] (default
+    T // ckpt_every slots). Returns (o [T,H,dv], S_final or None, S_ckpt or None)."""
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.shape[0] - 1
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_prefill_varlen needs GPU tensors")
+    if N < 0:
+        raise ValueError("cu_seqlens needs N + 1 >= 1 entries")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (T, H, dk), dt, dev)
+    _check(k, "k", (T, H, dk), dt, dev)
+    _check(v, "v", (T, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (T, H, dv), dt, dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
+    if ckpt_every > 0:
+        if ckpt_slots is None:
+            ckpt_slots = S_ckpt.shape[0] if S_ckpt is not None else max(T // ckpt_every, 1)
+        if S_ckpt is None:
+            S_ckpt = torch.empty((ckpt_slots, H, dk, dv), dtype=torch.float32, device=dev)
+        _check(S_ckpt, "S_ckpt", (ckpt_slots, H, dk, dv), torch.float32, dev)
+    else:
+        ckpt_slots, S_ckpt = 0, None
+    ws_bytes = kda_prefill_varlen_workspace_size(N, T, H, dk, dv, dt, chunk)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), N, T, H,
+                                dk, dv, _DTYPES[dt], chunk, _ptr(S_ckpt), int(ckpt_every),
+                                int(ckpt_slots), _ptr(workspace), wsz, _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_varlen")
+    return o, S_final, S_ckpt
 
 
 def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

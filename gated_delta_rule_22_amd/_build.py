@@ -19,7 +19,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill_generic.hip", "kda_prefill_mfma.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill_generic.hip", "kda_prefill_mfma.hip",
+           "kda_varlen.hip"]
 
 
 def _compile(src: str) -> str:

@@ -13,6 +13,16 @@ namespace {
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 0 || c == 16 || c == 32 || c == 64; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int kChunk = 64;   // chunk numbering of the MFMA path and checkpoint granularity
+
+// Chunks in the numbering of a packed call: sum_i ceil(len_i / 64) over N
+// sequences of T tokens in all is at most (T + 63 N) / 64.
+size_t varlen_chunk_bound(int N, int T) {
+    return ((size_t)T + (size_t)N * (kChunk - 1)) / kChunk;
+}
+size_t varlen_table_bytes(int N) { return align256((3 * (size_t)N + 3) * sizeof(int)); }
 
 struct Range {
     uintptr_t lo = 0, hi = 0;  // [lo, hi)
@@ -50,7 +60,8 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype
                                   int chunk) {
     if (B <= 0 || T <= 0 || H <= 0 || dtype != KDA_BF16) return 0;
     if (!kda::prefill_mfma_supported(dk, dv, chunk)) return 0;
-    return kda::prefill_mfma_workspace(B, T, H);
+    const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
+    return kda::prefill_mfma_workspace((long)B * H, nch, H);
 }
 
 kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
@@ -103,11 +114,107 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
-        e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, ws, st);
+    const kda::SeqLayout sq{nullptr, B, T, kChunk, 0};
+    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
+        const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
+        if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
+        e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H, (int)nch,
+                                     ws, nullptr, 0, st);
+    } else {
+        e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
+                                        S_final, sq, H, dk, dv, chunk ? chunk : 64, nullptr, 0,
+                                        st);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int dv,
+                                         kda_dtype dtype, int chunk) {
+    if (N <= 0 || T_total < 0 || H <= 0) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return 0;
+    size_t need = varlen_table_bytes(N);
+    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk))
+        need += kda::prefill_mfma_workspace((long)N * H, varlen_chunk_bound(N, T_total), H);
+    return need;
+}
+
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta,
+                              const float* S0, void* o, float* S_final,
+                              const int* cu_seqlens, int N, int T_total, int H, int dk, int dv,
+                              kda_dtype dtype, int chunk,
+                              float* S_ckpt, int ckpt_every, int ckpt_slots,
+                              void* ws, size_t ws_bytes, void* stream) {
+    if (N < 0 || T_total < 0 || H < 0 || ckpt_every < 0 || ckpt_slots < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (ckpt_every % kChunk != 0) return KDA_ERR_INVALID_ARG;
+    if (ckpt_every > 0 && (S_ckpt == nullptr || ckpt_slots == 0)) return KDA_ERR_INVALID_ARG;
+    if (ckpt_every == 0) {   // no checkpoints: S_ckpt and ckpt_slots are ignored
+        S_ckpt = nullptr;
+        ckpt_slots = 0;
+    }
+    if (N == 0 || H == 0) return KDA_OK;
+    if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return KDA_ERR_INVALID_ARG;
+    if (N > INT32_MAX / 4 || varlen_chunk_bound(N, T_total) > (size_t)INT32_MAX)
+        return KDA_ERR_INVALID_ARG;
+
+    const size_t elt = dtype == KDA_BF16 ? 2 : 4;
+    size_t tok = (size_t)T_total;
+    if (!mul_ok(tok, (size_t)H)) return KDA_ERR_INVALID_ARG;
+    size_t nk = tok, nv = tok, ns = (size_t)N * (size_t)H, nc = (size_t)ckpt_slots * (size_t)H;
+    if (!mul_ok(nk, (size_t)dk) || !mul_ok(nv, (size_t)dv) || !mul_ok(ns, (size_t)dk * dv) ||
+        !mul_ok(nc, (size_t)dk * dv))
+        return KDA_ERR_INVALID_ARG;
+    if (nk > (SIZE_MAX >> 3) || nv > (SIZE_MAX >> 3) || ns > (SIZE_MAX >> 3) ||
+        nc > (SIZE_MAX >> 3))
+        return KDA_ERR_INVALID_ARG;
+
+    if (T_total > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_final, S_ckpt};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    const size_t ws_need = kda_prefill_varlen_workspace_size(N, T_total, H, dk, dv, dtype, chunk);
+    if (ws == nullptr || ws_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return KDA_ERR_INVALID_ARG;
+
+    const bool has_t = T_total > 0;
+    const Range rq(q, has_t ? nk * elt : 0), rk(k, has_t ? nk * elt : 0),
+        rv(v, has_t ? nv * elt : 0);
+    const Range rla(log_alpha, has_t ? nk * 4 : 0), rb(beta, has_t ? tok * 4 : 0);
+    const Range rs0(S0, S0 ? ns * 4 : 0), rcu(cu_seqlens, ((size_t)N + 1) * 4);
+    const Range ro(o, has_t ? nv * elt : 0), rsf(S_final, S_final ? ns * 4 : 0),
+        rck(S_ckpt, S_ckpt ? nc * 4 : 0), rws(ws, ws_need);
+    const Range inputs[] = {rq, rk, rv, rla, rb, rs0, rcu};
+    const Range outputs[] = {ro, rsf, rck, rws};
+    for (const Range& out : outputs)
+        for (const Range& in : inputs)
+            if (overlap(out, in)) {
+                // the only permitted overlap: S_final is exactly S0
+                if (&out == &outputs[1] && &in == &inputs[5] && rsf.lo == rs0.lo) continue;
+                return KDA_ERR_INVALID_ARG;
+            }
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(outputs[a], outputs[b])) return KDA_ERR_INVALID_ARG;
+
+    hipStream_t st = (hipStream_t)stream;
+    int* tab = (int*)ws;
+    hipError_t e = kda::launch_varlen_table(cu_seqlens, N, T_total, kChunk, ckpt_every, tab, st);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    const kda::SeqLayout sq{tab, N, T_total, kChunk, ckpt_every};
+    // With no tokens every sequence is empty and only S_final = S0 remains:
+    // the generic kernel does that without touching a chunk record.
+    if (dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
+        e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H,
+                                     (int)varlen_chunk_bound(N, T_total),
+                                     (char*)ws + varlen_table_bytes(N), S_ckpt, ckpt_slots, st);
     else
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
-                                        S_final, B, T, H, dk, dv, chunk ? chunk : 64, st);
+                                        S_final, sq, H, dk, dv, chunk ? chunk : 64, S_ckpt,
+                                        ckpt_slots, st);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

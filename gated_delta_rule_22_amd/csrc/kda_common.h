@@ -67,6 +67,33 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Sequence layout of a prefill call. Tokens are packed along one axis
+// ([tokens, H, d] row-major); sequence i covers tokens
+// [start(i), start(i) + len(i)) and is cut into chunks of C tokens from its
+// own start. Either N sequences of T tokens each (tab == nullptr), or a table
+// built on the device from cumulative offsets (launch_varlen_table):
+//   tab[0 .. N]           offsets, non-decreasing, inside [0, T]
+//   tab[N+1 .. 2N+1]      first chunk of each sequence in a numbering of all
+//                         chunks (exclusive prefix sum; tab[2N+1] = total)
+//   tab[2N+2 .. 3N+2]     first checkpoint slot of each sequence
+// K is the checkpoint interval in tokens (a multiple of C), 0 for none:
+// sequence i has len(i) / K checkpoints, the states after K, 2K, ... tokens.
+struct SeqLayout {
+    const int* tab;
+    int N;   // sequences
+    int T;   // tokens per sequence (no table) or in all (table)
+    int C;   // chunk length of the chunk numbering
+    int K;   // checkpoint interval, 0 = none
+    __device__ long start(int i) const { return tab ? (long)tab[i] : (long)i * T; }
+    __device__ int len(int i) const { return tab ? tab[i + 1] - tab[i] : T; }
+    __device__ long chunk0(int i) const {
+        return tab ? (long)tab[N + 1 + i] : (long)i * ((T + C - 1) / C);
+    }
+    __device__ long ckpt0(int i) const {
+        return tab ? (long)tab[2 * N + 2 + i] : (K ? (long)i * (T / K) : 0);
+    }
+};
+
 // Natural exponential through the hardware exp2 (v_exp_f32).
 __device__ __forceinline__ float exp_e(float x) { return __expf(x); }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "kda_common.h"
+
 namespace kda {
 
 // Decode step over B*H heads.
@@ -18,19 +20,29 @@ hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, cons
                                void* o, const int* n_commit, int BH, int H, int ntok,
                                hipStream_t st);
 
-// Generic chunked prefill (fp32 arithmetic, any supported dk/dv/chunk, fp32 or bf16 I/O).
+// Sequence table of a packed variable-length call (layout: SeqLayout) from
+// device offsets cu[0..N], into tab (3N + 3 ints of device memory).
+hipError_t launch_varlen_table(const int* cu, int N, int T, int C, int K, int* tab,
+                               hipStream_t st);
+
+// Generic chunked prefill (fp32 arithmetic, any supported dk/dv/chunk, fp32 or
+// bf16 I/O) over the sequences of `sq`; checkpoints when S_ckpt and sq.K are set.
 hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, const void* v,
                                   const float* la, const float* beta, const float* S0,
-                                  void* o, float* S_final, int B, int T, int H, int dk,
-                                  int dv, int chunk, hipStream_t st);
+                                  void* o, float* S_final, const SeqLayout& sq, int H, int dk,
+                                  int dv, int chunk, float* S_ckpt, int ck_slots, hipStream_t st);
 
-// bf16 MFMA chunked prefill for dk = dv = 128, chunk 64. For few heads it
-// runs a chunk-parallel prep kernel and a state kernel that communicate
-// through `ws` (prefill_mfma_workspace() bytes); otherwise one fused kernel.
+// bf16 MFMA chunked prefill for dk = dv = 128, chunk 64, over the sequences
+// of `sq` (sq.C = 64). Below 128 sequence-heads it runs a chunk-parallel prep
+// kernel and a state kernel that communicate through `ws`
+// (prefill_mfma_workspace() bytes for nch_all chunks in the numbering);
+// otherwise one fused kernel.
 bool prefill_mfma_supported(int dk, int dv, int chunk);
-size_t prefill_mfma_workspace(int B, int T, int H);
+bool prefill_mfma_split(long pairs);
+size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H);
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
                                const float* beta, const float* S0, void* o, float* S_final,
-                               int B, int T, int H, void* ws, hipStream_t st);
+                               const SeqLayout& sq, int H, int nch_all, void* ws,
+                               float* S_ckpt, int ck_slots, hipStream_t st);
 
 }  // namespace kda

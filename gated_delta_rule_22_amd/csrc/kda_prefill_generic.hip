@@ -3,7 +3,9 @@
 // Serves the fp32-input path (where a 1e-5 match to the fp64 recurrence is
 // required, so no bf16 rounding may enter) and any dk/dv/chunk the bf16 MFMA
 // kernel does not implement. One workgroup per (batch, head); the state lives
-// in LDS for the whole sequence.
+// in LDS for the whole sequence. Sequences follow a SeqLayout (fixed-length
+// batches or a packed variable-length table), and the state after every K
+// tokens of a sequence can be stored as a checkpoint.
 //
 // Per chunk of n tokens with starting state S ("Kimi K3: the manos...",
 // section "FlashKDA Algorithm"; cum_t is the inclusive sum of log-decays from
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const float* S0, T* __restrict__ o, float* S_final,
-    int Tlen, int H, int dk, int dv, int C)
+    SeqLayout sq, int H, int dk, int dv, int C, float* __restrict__ S_ckpt, int ck_slots)
 {
     __shared__ float sS[gen::kMaxD * gen::kMaxD];
     __shared__ float sQ[gen::kTile], sK[gen::kTile], sCum[gen::kTile], sKd[gen::kTile];
@@ -44,8 +46,12 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
     const int tid = threadIdx.x;
     const int NT = blockDim.x;
     const int bh = blockIdx.x;
-    const int b = bh / H, h = bh - b * H;
+    const int b = bh / H, h = bh - b * H;   // sequence b, head h
     const size_t soff = (size_t)bh * dk * dv;
+    const long tok0 = sq.start(b);
+    const int Tlen = sq.len(b);
+    const bool ckpt = S_ckpt != nullptr && sq.K > 0;
+    const long ck0 = ckpt ? sq.ckpt0(b) : 0;
 
     for (int i = tid; i < dk * dv; i += NT) sS[i] = S0 ? S0[soff + i] : 0.f;
     __syncthreads();
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
     for (int c0 = 0; c0 < Tlen; c0 += C) {
         const int n = min(C, Tlen - c0);
         // token-head row index of token t of this chunk
-        auto row = [&](int t) -> size_t { return ((size_t)b * Tlen + c0 + t) * H + h; };
+        auto row = [&](int t) -> size_t { return ((size_t)tok0 + c0 + t) * H + h; };
 
         for (int i = tid; i < n * dk; i += NT) {
             const int t = i / dk, d = i - t * dk;
@@ -144,6 +150,15 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
             sS[i] = acc;
         }
         __syncthreads();
+
+        // checkpoint j after j * K tokens (C divides K, so chunk ends meet it)
+        if (ckpt && (c0 + n) % sq.K == 0) {
+            const long slot = ck0 + (c0 + n) / sq.K - 1;
+            if (slot < ck_slots) {
+                float* dst = S_ckpt + ((size_t)slot * H + h) * dk * dv;
+                for (int i = tid; i < dk * dv; i += NT) dst[i] = sS[i];
+            }
+        }
     }
 
     if (S_final)
@@ -152,8 +167,8 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
 
 hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, const void* v,
                                   const float* la, const float* beta, const float* S0,
-                                  void* o, float* S_final, int B, int T, int H, int dk,
-                                  int dv, int chunk, hipStream_t st)
+                                  void* o, float* S_final, const SeqLayout& sq, int H, int dk,
+                                  int dv, int chunk, float* S_ckpt, int ck_slots, hipStream_t st)
 {
     // Largest chunk whose tiles fit the LDS budget; the chunk length changes
     // only the blocking, never the result.
@@ -161,15 +176,15 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
     const int dmax = dk > dv ? dk : dv;
     while (C > 1 && C * dmax > gen::kTile) C >>= 1;
     if (C > gen::kMaxC) C = gen::kMaxC;
-    const dim3 grid((unsigned)(B * H));
+    const dim3 grid((unsigned)((long)sq.N * H));
     if (bf16_io)
         hipLaunchKernelGGL(prefill_generic_kernel<bf16>, grid, dim3(gen::kThreads), 0, st,
                            (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
-                           (bf16*)o, S_final, T, H, dk, dv, C);
+                           (bf16*)o, S_final, sq, H, dk, dv, C, S_ckpt, ck_slots);
     else
         hipLaunchKernelGGL(prefill_generic_kernel<float>, grid, dim3(gen::kThreads), 0, st,
                            (const float*)q, (const float*)k, (const float*)v, la, beta, S0,
-                           (float*)o, S_final, T, H, dk, dv, C);
+                           (float*)o, S_final, sq, H, dk, dv, C, S_ckpt, ck_slots);
     return hipGetLastError();
 }
 

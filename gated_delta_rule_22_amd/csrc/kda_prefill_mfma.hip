@@ -145,7 +145,8 @@ struct Inputs {
     float beta;
 };
 
-// Load chunk c's inputs. Thread (wave = token range, lane = channel pair).
+// Load chunk c of a sequence's inputs. Thread (wave = token range, lane =
+// channel pair).
 // Loads are unconditional (tail tokens re-read the last token) and the raw
 // values are kept as loaded: tail tokens are zeroed where they are consumed,
 // so no instruction waits on a load before the next chunk is needed.
@@ -154,14 +155,15 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
                                             const bf16* __restrict__ k,
                                             const bf16* __restrict__ v,
                                             const float* __restrict__ log_alpha,
-                                            const float* __restrict__ beta, int b, int h, int T,
-                                            int H, int c, int col0)
+                                            const float* __restrict__ beta, long tok0, int len,
+                                            int h, int H, int c, int col0)
 {
     constexpr int TPT = C / NW;
     constexpr int VPR = DVB / 8;   // 16-byte pieces per value row
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int t0 = wave * TPT;
-    auto row = [&](int tok) -> size_t { return ((size_t)b * T + min(tok, T - 1)) * H + h; };
+    // token tok of the sequence starting at tok0 (len > 0 tokens)
+    auto row = [&](int tok) -> size_t { return ((size_t)tok0 + min(tok, len - 1)) * H + h; };
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
         const size_t base = row(c * C + t0 + j) * DK + 2 * lane;
@@ -633,12 +635,25 @@ __device__ __forceinline__ void store_o(const f32x4 (&O)[4], bf16* stage, bf16* 
 }  // namespace mf
 
 // ---------------------------------------------------------------------------
-// Fused kernel: one workgroup per (batch*head, value block of 16*NW columns).
-template <int NW>
+// Store this wave's part of a state block (Sacc[m][i] = row 16m + 4g + i,
+// column ncol) to the [128][128] fp32 block at dst.
+__device__ __forceinline__ void store_state(float* dst, const f32x4 (&Sacc)[8], int g, int ncol) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * m + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+}
+
+// Fused kernel: one workgroup per (sequence*head, value block of 16*NW
+// columns). With CKPT it also stores the state after every sq.K tokens of the
+// sequence to checkpoint slot sq.ckpt0(i) + j - 1 (slots >= ck_slots are
+// dropped).
+template <int NW, bool CKPT>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const float* S0, bf16* __restrict__ o, float* S_final, int T, int H, int NVB)
+    const float* S0, bf16* __restrict__ o, float* S_final, SeqLayout sq, int H, int NVB,
+    float* __restrict__ S_ckpt, int ck_slots)
 {
     using namespace mf;
     constexpr int DVB = NW * 16;
@@ -652,6 +667,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const int b = bh / H, h = bh - b * H;
     const int col0 = vb * DVB;
     const int ncol = col0 + 16 * wave + r;
+    const long tok0 = sq.start(b);
+    const int len = sq.len(b);
 
     f32x4 Sacc[8];
     const size_t sbase = (size_t)bh * DK * 128;
@@ -666,11 +683,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     }
 
     Inputs<NW> in;
-    const int nchunks = (T + C - 1) / C;
-    if (nchunks > 0) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, 0, col0);
+    const int nchunks = (len + C - 1) / C;
+    const int ck_every = CKPT ? sq.K / C : 1;   // chunks per checkpoint
+    const long ck0 = CKPT ? sq.ckpt0(b) : 0;
+    if (nchunks > 0) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, tok0, len, h, H, 0, col0);
 
     for (int c = 0; c < nchunks; ++c) {
-        const int ntok = T - c * C;
+        const int ntok = len - c * C;
         lds_barrier();
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
@@ -680,10 +699,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         // next chunk's inputs; with 8 waves, waves 4-7 (lighter Gram work)
         // fetch after stage 2, so their fetches queue while the inverses finish
         const bool early_fetch = NW < 8 || wave < 4;
-        if (c + 1 < nchunks && early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
+        if (c + 1 < nchunks && early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, tok0, len, h, H, c + 1, col0);
         lds_barrier();
         stage2<NW>(sm, fast);
-        if (c + 1 < nchunks && !early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, col0);
+        if (c + 1 < nchunks && !early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, tok0, len, h, H, c + 1, col0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
@@ -692,23 +711,72 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         state_pass<(NW < 8)>(Sacc, U0, sm.NWop, sm.Qd, sm.Mop, sm.KrT, sm.alast, O);
         // staging slots: waves 0-4 in Kd, 5-7 in Ki (both dead until the next chunk)
         bf16* stage = (wave < 5) ? sm.Kd + wave * (C * OTS) : sm.Ki + (wave - 5) * (C * OTS);
-        store_o(O, stage, o, ((size_t)b * T + (size_t)c * C) * H + h, (size_t)H, col0 + 16 * wave, ntok);
+        store_o(O, stage, o, ((size_t)tok0 + (size_t)c * C) * H + h, (size_t)H, col0 + 16 * wave, ntok);
+        if (CKPT && ntok >= C && (c + 1) % ck_every == 0) {
+            const long slot = ck0 + (c + 1) / ck_every - 1;
+            if (slot < ck_slots) store_state(S_ckpt + ((size_t)slot * H + h) * DK * 128, Sacc, g, ncol);
+        }
     }
 
-    if (S_final) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S_final[sbase + (size_t)(16 * m + 4 * g + i) * 128 + ncol] = Sacc[m][i];
-    }
+    if (S_final) store_state(S_final + sbase, Sacc, g, ncol);
 }
 
-// Prep kernel: chunks [c0, c0 + cpw) of one head; writes operand records.
+// Chunk numbering of the prep kernel, for fewer than 128 sequences: chunk gc
+// of all chunks -> first token and length of its sequence, chunk within it.
+struct ChunkPos {
+    long tok0;
+    int len, c;
+};
+template <bool kTable>
+struct ChunkMap {
+    SeqLayout sq;
+    int nch;              // without a table: chunks per sequence
+    int off[2], cst[2];   // with a table: offset and first chunk of entries lane, 64 + lane
+    __device__ explicit ChunkMap(const SeqLayout& s) : sq(s), nch((s.T + mf::C - 1) / mf::C) {
+        if (kTable) {
+            const int lane = threadIdx.x & 63;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int j = min(lane + 64 * u, s.N);   // entries past N repeat entry N
+                off[u] = s.tab[j];
+                cst[u] = (lane + 64 * u <= s.N) ? s.tab[s.N + 1 + j] : 0x7fffffff;
+            }
+        }
+    }
+    // entry j (wave-uniform) of a lane-distributed array
+    __device__ int entry(const int (&x)[2], int j) const {
+        return j < 64 ? __builtin_amdgcn_readlane(x[0], j) : __builtin_amdgcn_readlane(x[1], j - 64);
+    }
+    __device__ int total() const { return kTable ? entry(cst, sq.N) : sq.N * nch; }
+    __device__ ChunkPos at(int gc) const {
+        if (!kTable) {
+            const int i = gc / nch;
+            return {(long)i * sq.T, sq.T, gc - i * nch};
+        }
+        // the sequence is the last entry whose first chunk is <= gc
+        const int i = __builtin_popcountll(__builtin_amdgcn_ballot_w64(cst[0] <= gc)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(cst[1] <= gc)) - 1;
+        const int o0 = entry(off, i);
+        return {(long)o0, entry(off, i + 1) - o0, gc - entry(cst, i)};
+    }
+    // position of chunk gc + 1 given that of chunk gc
+    __device__ ChunkPos next(const ChunkPos& p, int gc) const {
+        if (!kTable) {
+            if (p.c + 1 < nch) return {p.tok0, p.len, p.c + 1};
+            return {p.tok0 + sq.T, p.len, 0};
+        }
+        return at(gc + 1);
+    }
+};
+
+// Prep kernel: chunks [gc0, gc0 + cpw) of the chunk numbering, head h;
+// writes the operand record of chunk gc at record h * nch_all + gc. kTable:
+// the sequences come from a device table (fewer than 128 of them).
+template <bool kTable>
 __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    char* __restrict__ ws, int T, int H, int cpw)
+    char* __restrict__ ws, SeqLayout sq, int H, int cpw, int nch_all)
 {
     using namespace mf;
     constexpr int NW = 8, DVB = 128;
@@ -716,17 +784,22 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     __shared__ bf16 sV[C * (DVB + 8)];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int nchunks = (T + C - 1) / C;
-    const int ngrp = (nchunks + cpw - 1) / cpw;
-    const int bh = blockIdx.x / ngrp;
-    const int c0 = (blockIdx.x - bh * ngrp) * cpw;
-    const int c1 = min(c0 + cpw, nchunks);
-    const int b = bh / H, h = bh - b * H;
+    const int ngrp = (nch_all + cpw - 1) / cpw;
+    const int h = blockIdx.x / ngrp;
+    const int gc0 = (blockIdx.x - h * ngrp) * cpw;
+    const ChunkMap<kTable> map(sq);
+    const int gc1 = min(gc0 + cpw, map.total());
 
     Inputs<NW> in;
-    if (c0 < c1) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c0, 0);
-    for (int c = c0; c < c1; ++c) {
-        const int ntok = T - c * C;
+    ChunkPos p{0, 1, 0};
+    if (gc0 < gc1) {
+        p = map.at(gc0);
+        load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, p.tok0, p.len, h, H, p.c, 0);
+    }
+    for (int gc = gc0; gc < gc1; ++gc) {
+        const int ntok = p.len - p.c * C;
+        const bool more = gc + 1 < gc1;
+        const ChunkPos pn = more ? map.next(p, gc) : p;
         lds_barrier();
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
@@ -735,15 +808,16 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         else stage1b<NW, false>(sm, in, ntok, fast);
         // next chunk's inputs: waves 0-3 now; waves 4-7 (lighter Gram work)
         // after stage 2, so their fetches queue while the inverses finish
-        if (c + 1 < c1 && wave < 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
+        if (more && wave < 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         stage2<NW>(sm, fast);
-        if (c + 1 < c1 && wave >= 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, b, h, T, H, c + 1, 0);
+        if (more && wave >= 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
         lds_barrier();
-        char* rec = ws + ((size_t)bh * nchunks + c) * REC_BYTES;
+        p = pn;
+        char* rec = ws + ((size_t)h * nch_all + gc) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
         // 54 A operands, spread over the waves: 16 B per lane each. Seven per
         // wave; waves 6, 7 store their sixth operand twice (same data, same
@@ -780,7 +854,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     }
 }
 
-// State kernel: one workgroup of twelve waves per (batch*head, 16 value
+// State kernel: one workgroup of twelve waves per (sequence*head, 16 value
 // columns). Each wave has one role, so the chunk-to-chunk chain is two short
 // MFMA passes and every wave loads only the few operands it uses:
 //   waves 0-3  (U): U = U0 - W S for token tile w                 (-W: 4 KB)
@@ -803,9 +877,12 @@ namespace mf {
 constexpr int PF = 4;   // operand sets in flight per wave
 }
 
+// With CKPT the S waves also store the state after every sq.K tokens of the
+// sequence to checkpoint slot sq.ckpt0(i) + j - 1 (slots >= ck_slots are dropped).
+template <bool CKPT>
 __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
     const char* __restrict__ ws, const float* S0, bf16* __restrict__ o, float* S_final,
-    int T, int H, int BH)
+    SeqLayout sq, int H, int BH, int nch_all, float* __restrict__ S_ckpt, int ck_slots)
 {
     using namespace mf;
     __shared__ bf16x8 sSB[4][64];        // S as four B operands (32-deep steps)
@@ -818,14 +895,20 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
     const int bh = grp * 8 + (blockIdx.x & 7);
     const int ct = (blockIdx.x >> 3) & 7;          // value column tile
     if (bh >= BH) return;                          // whole workgroup: uniform
-    const int b = bh / H, h = bh - b * H;
+    const int b = bh / H, h = bh - b * H;          // sequence b, head h
     const int ncol = 16 * ct + r;
+    const long tok0 = sq.start(b);
+    const int T = sq.len(b);
     const int nchunks = (T + C - 1) / C;
     const size_t sbase = (size_t)bh * DK * 128;
+    // An empty sequence walks no chunk: its waves fetch record 0 of the
+    // workspace (unused) and the S waves store S_final = S0.
+    const size_t rbase = nchunks > 0 ? (size_t)h * nch_all + sq.chunk0(b) : 0;
+    const int clast = max(nchunks - 1, 0);
 
     // record of chunk c, clamped: fetches past the end reload the last one
     auto rec = [&](int c) -> const char* {
-        return ws + ((size_t)bh * nchunks + min(c, nchunks - 1)) * REC_BYTES;
+        return ws + (rbase + min(c, clast)) * REC_BYTES;
     };
     auto op = [&](const char* rp, int off) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(rp + off + lane * 16);
@@ -888,6 +971,9 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
             Sacc[0] = zero4();
             Sacc[1] = zero4();
         }
+        const int ck_every = CKPT ? sq.K / C : 1;   // chunks per checkpoint
+        int ck_left = ck_every;                      // chunks until the next one
+        int ck_slot = CKPT ? (int)sq.ckpt0(b) : 0;   // its slot
         struct Ops { bf16x8 k[4]; f32x4 al[2]; };
         auto load = [&](Ops& x, int c) {
             const char* rp = rec(c);
@@ -915,6 +1001,18 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
                 Sacc[m] = mma32(x.k[2 * m + 1], UB1, Sacc[m]);
             }
             sSB[s][lane] = pack8(Sacc[0], Sacc[1]);
+            if (CKPT && --ck_left == 0) {                   // checkpoint after chunk c
+                ck_left = ck_every;
+                if ((c + 1) * C <= T && ck_slot < ck_slots) {
+                    float* dst = S_ckpt + ((size_t)ck_slot * H + h) * DK * 128 +
+                                 (16 * m0 + 4 * g) * 128 + ncol;
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dst[(16 * m + i) * 128] = Sacc[m][i];
+                }
+                ++ck_slot;
+            }
         });
         if (S_final) {
 #pragma unroll
@@ -1004,7 +1102,7 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
                 if (decltype(full)::value || 16 * I < nt) {
                     const int t = decltype(full)::value ? 16 * I + tt : min(16 * I + tt, nt - 1);
                     const uint2 v = *reinterpret_cast<const uint2*>(&tile[(t - 16 * I) * 16 + tc]);
-                    *reinterpret_cast<uint2*>(o + (((size_t)b * T + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc) = v;
+                    *reinterpret_cast<uint2*>(o + (((size_t)tok0 + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc) = v;
                 }
             });
         };
@@ -1022,48 +1120,52 @@ bool prefill_mfma_supported(int dk, int dv, int chunk) {
     return dk == 128 && dv == 128 && (chunk == 64 || chunk == 0);
 }
 
-size_t prefill_mfma_workspace(int B, int T, int H) {
-    const long heads = (long)B * H;
-    if (heads >= kSplitBelowHeads || T <= 0) return 0;
-    const size_t nchunks = ((size_t)T + mf::C - 1) / mf::C;
-    return (size_t)heads * nchunks * mf::REC_BYTES;
+bool prefill_mfma_split(long pairs) { return pairs < kSplitBelowHeads; }
+
+size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H) {
+    if (!prefill_mfma_split(pairs)) return 0;
+    return (size_t)H * nch_all * mf::REC_BYTES;
 }
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
                                const float* beta, const float* S0, void* o, float* S_final,
-                               int B, int T, int H, void* ws, hipStream_t st)
+                               const SeqLayout& sq, int H, int nch_all, void* ws,
+                               float* S_ckpt, int ck_slots, hipStream_t st)
 {
-    const long heads = (long)B * H;
-    if (heads >= 256) {
-        hipLaunchKernelGGL(prefill_fused_kernel<8>, dim3((unsigned)heads), dim3(512), 0, st,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
-                           (bf16*)o, S_final, T, H, 1);
+    const long pairs = (long)sq.N * H;
+    const bool ck = S_ckpt != nullptr && sq.K > 0 && ck_slots > 0;
+    if (!prefill_mfma_split(pairs)) {
+        const bool wide = pairs >= 256;   // one 8-wave workgroup per pair, else two of 4 waves
+        const dim3 grid((unsigned)(wide ? pairs : pairs * 2)), block(wide ? 512 : 256);
+        const int nvb = wide ? 1 : 2;
+        auto kern = wide ? (ck ? prefill_fused_kernel<8, true> : prefill_fused_kernel<8, false>)
+                         : (ck ? prefill_fused_kernel<4, true> : prefill_fused_kernel<4, false>);
+        hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                           (const bf16*)v, la, beta, S0, (bf16*)o, S_final, sq, H, nvb, S_ckpt,
+                           ck_slots);
         return hipGetLastError();
     }
-    if (heads >= kSplitBelowHeads) {
-        hipLaunchKernelGGL(prefill_fused_kernel<4>, dim3((unsigned)(heads * 2)), dim3(256), 0, st,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
-                           (bf16*)o, S_final, T, H, 2);
-        return hipGetLastError();
+    // few sequence-heads: chunk-parallel prep, then the state walk
+    if (nch_all > 0) {
+        const long work = (long)H * nch_all;
+        int cpw = (int)((work + 255) / 256);          // about one workgroup per CU
+        if (cpw < 1) cpw = 1;
+        const long ngrp = (nch_all + cpw - 1) / cpw;
+        hipLaunchKernelGGL(sq.tab ? prefill_prep_kernel<true> : prefill_prep_kernel<false>,
+                           dim3((unsigned)(H * ngrp)), dim3(512), 0, st,
+                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, (char*)ws,
+                           sq, H, cpw, nch_all);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    // few heads: chunk-parallel prep, then the state walk
-    const long nchunks = (T + mf::C - 1) / mf::C;
-    const long work = heads * nchunks;
-    int cpw = (int)((work + 255) / 256);          // about one workgroup per CU
-    if (cpw < 1) cpw = 1;
-    const long ngrp = (nchunks + cpw - 1) / cpw;
-    hipLaunchKernelGGL(prefill_prep_kernel, dim3((unsigned)(heads * ngrp)), dim3(512), 0, st,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, (char*)ws, T, H,
-                       cpw);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long groups = (heads + 7) / 8;   // 8 heads x 8 column tiles per group of 64 blocks
+    const long groups = (pairs + 7) / 8;   // 8 pairs x 8 column tiles per group of 64 blocks
     // A workspace that outgrows the last-level cache (256 MB) streams from
     // HBM: add the L2 prefetch wave (thirteenth wave) for it.
-    const size_t ws_bytes = (size_t)heads * nchunks * mf::REC_BYTES;
+    const size_t ws_bytes = prefill_mfma_workspace(pairs, (size_t)nch_all, H);
     const unsigned threads = ws_bytes > (size_t(128) << 20) ? 832u : 768u;
-    hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)(groups * 64)), dim3(threads), 0, st,
-                       (const char*)ws, S0, (bf16*)o, S_final, T, H, (int)heads);
+    hipLaunchKernelGGL(ck ? prefill_state_kernel<true> : prefill_state_kernel<false>,
+                       dim3((unsigned)(groups * 64)), dim3(threads), 0, st, (const char*)ws, S0,
+                       (bf16*)o, S_final, sq, H, (int)pairs, nch_all, S_ckpt, ck_slots);
     return hipGetLastError();
 }
 

@@ -90,6 +90,55 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Bytes of device workspace kda_prefill_varlen needs for these sizes (never 0
+ * for N, H > 0: it always holds the sequence table). Returns 0 for arguments
+ * it would reject.
+ */
+size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int dv,
+                                         kda_dtype dtype, int chunk);
+
+/*
+ * Packed variable-length prefill with state checkpoints. Serving packs the
+ * prompts of N requests along one token axis and keeps each request's state
+ * at its prompt end and at coarse token intervals, since a state per token
+ * would grow with the length ("Kimi K3: the manos...", section "KDA Prefix
+ * Cache Management"; the trillion-scale architecture page, section 6:
+ * checkpoints on a 512-token hash grid).
+ *
+ *   q, k, log_alpha [T_total,H,dk]; v, o [T_total,H,dv]; beta [T_total,H]
+ *            (the kda_prefill_fwd layout with B = 1)
+ *   cu_seqlens  device int32 [N+1], 4-byte aligned: sequence i is tokens
+ *            [cu[i], cu[i+1]). The recurrence restarts at each sequence from
+ *            S0[i]. Offsets are read on the device and not validated on the
+ *            host: they are meant to be non-decreasing from cu[0] = 0 to
+ *            cu[N] = T_total. Otherwise each is clamped into [0, T_total] and
+ *            raised to the running maximum, which keeps every access inside
+ *            the buffers (output rows outside all sequences are not written).
+ *            Empty sequences are allowed: S_final[i] = S0[i] (or 0).
+ *   S0, S_final [N,H,dk,dv] fp32: as in kda_prefill_fwd (NULL S0 = zeros,
+ *            NULL S_final = skip, S_final may be exactly S0).
+ *   ckpt_every  0, or a multiple of 64: the state after every ckpt_every
+ *            tokens of each sequence (counted from its start) is stored to
+ *            S_ckpt [ckpt_slots,H,dk,dv] fp32. Sequence i's checkpoints j = 1
+ *            .. len_i / ckpt_every take slots c_i + j - 1, where c_i is the
+ *            sum of len / ckpt_every over the sequences before i. Slots
+ *            at or past ckpt_slots are not written. T_total / ckpt_every
+ *            slots always suffice. With ckpt_every = 0, S_ckpt and
+ *            ckpt_slots are ignored.
+ *   ws, ws_bytes  device workspace, 256-byte aligned, at least
+ *            kda_prefill_varlen_workspace_size() bytes (required).
+ * Outputs (o, S_final, S_ckpt, ws) must not overlap each other or an input.
+ * The result for each sequence equals kda_prefill_fwd on that sequence alone.
+ */
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta,
+                              const float* S0, void* o, float* S_final,
+                              const int* cu_seqlens, int N, int T_total, int H, int dk, int dv,
+                              kda_dtype dtype, int chunk,
+                              float* S_ckpt, int ckpt_every, int ckpt_slots,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One-token decode step (the recurrence above for a single t, the form
  * "Kimi K3: the manos..." section "FlashKDA Algorithm" gives as
  * u = beta (v - (D S)^T k), S = D S + k u^T, o^T = q^T S), updating S in

@@ -31,6 +31,7 @@ def declared_symbols():
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert set(syms) == {"kda_prefill_workspace_size", "kda_prefill_fwd",
+                         "kda_prefill_varlen_workspace_size", "kda_prefill_varlen",
                          "kda_decode_step", "kda_decode_multi", "kda_status_string"}
     for s in syms:
         assert hasattr(lib, s), s
@@ -136,6 +137,56 @@ def test_decode_multi_rejects(lib):
     assert multi(lib, o=P(5, 64)) == INVALID         # o inside S
     assert multi(lib, T=0) == OK                     # nothing to do
     assert multi(lib, B=0) == OK
+
+
+def varlen(lib, *, q=P(0), k=P(1), v=P(2), la=P(3), beta=P(4), S0=P(5), o=P(6), Sf=P(7),
+           cu=P(8), N=3, T=300, H=2, dk=128, dv=128, dt=1, chunk=64, ck=P(9), every=64,
+           slots=4, ws=P(10), ws_bytes=1 << 30):
+    lib.kda_prefill_varlen.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 7 + \
+        [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+         ctypes.c_void_p]
+    return lib.kda_prefill_varlen(q, k, v, la, beta, S0, o, Sf, cu, N, T, H, dk, dv, dt, chunk,
+                                  ck, every, slots, ws, ws_bytes, None)
+
+
+def test_varlen_workspace_query(lib):
+    f = lib.kda_prefill_varlen_workspace_size
+    f.restype = ctypes.c_size_t
+    tab = f(3, 300, 64, 128, 128, 1, 64)             # 192 sequence-heads: fused, table only
+    assert tab == 256
+    assert f(3, 300, 64, 128, 128, 0, 64) == 256     # fp32 path: table only
+    few = f(3, 300, 2, 128, 128, 1, 64)              # 6 sequence-heads: records too
+    assert few > tab and (few - tab) % (2 * ((300 + 3 * 63) // 64)) == 0
+    assert f(0, 300, 2, 128, 128, 1, 64) == 0
+    assert f(3, 300, 2, 48, 128, 1, 64) == 0         # unsupported
+
+
+def test_varlen_rejects(lib):
+    assert varlen(lib, N=-1) == INVALID
+    assert varlen(lib, T=-1) == INVALID
+    assert varlen(lib, dk=48) == UNSUPPORTED
+    assert varlen(lib, chunk=128) == UNSUPPORTED
+    assert varlen(lib, every=100) == INVALID          # not a multiple of 64
+    assert varlen(lib, every=-64) == INVALID
+    assert varlen(lib, ck=None) == INVALID            # checkpoints without a buffer
+    assert varlen(lib, slots=0) == INVALID
+    assert varlen(lib, slots=-1) == INVALID
+    assert varlen(lib, cu=None) == INVALID
+    assert varlen(lib, cu=P(8, 2)) == INVALID         # cu_seqlens not 4-byte aligned
+    for name in ("q", "k", "v", "la", "beta", "o"):
+        assert varlen(lib, **{name: None}) == INVALID, name
+    for name in ("q", "k", "v", "la", "beta", "S0", "o", "Sf", "ck"):
+        assert varlen(lib, **{name: P(11, 4)}) == INVALID, name
+    assert varlen(lib, ws=None) == WORKSPACE
+    assert varlen(lib, ws_bytes=16) == WORKSPACE
+    assert varlen(lib, ws=P(10, 16)) == INVALID       # not 256-byte aligned
+    assert varlen(lib, o=P(8)) == INVALID             # o overlapping cu_seqlens
+    assert varlen(lib, ck=P(5, 256)) == INVALID       # checkpoints overlapping S0
+    assert varlen(lib, ck=P(7)) == INVALID            # checkpoints overlapping S_final
+    assert varlen(lib, ws=P(9)) == INVALID            # workspace overlapping checkpoints
+    assert varlen(lib, Sf=P(5, 256)) == INVALID       # partial overlap with S0
+    assert varlen(lib, N=0) == OK                     # nothing to do
+    assert varlen(lib, H=0) == OK
 
 
 def test_binding_rejects_cpu_tensors():

@@ -12,9 +12,12 @@ in HBM before timing; each timed step reads its own replica of the batch so
 the 256 MB last-level cache cannot hold the inputs between steps.
 
 Also reported in the same line: the decode workload (B=256, H=32, d=128, 1024
-sequential steps, fp32 state of 537 MB streamed per step) as "decode", the
-roofline of the dominant kernel timed with HIP events on its stream, and the
-fp64 CPU oracle timed on the host cores over a bounded sample.
+sequential steps, fp32 state of 537 MB streamed per step) as "decode", an
+8-token draft verified and committed from that state as "decode_multi", a
+packed batch of 18 prompts of mixed length (65,536 tokens, H=32) with state
+checkpoints every 512 tokens as "varlen", the roofline of the dominant kernel
+timed with HIP events on its stream, and the fp64 CPU oracle timed on the host
+cores over a bounded sample.
 """
 from __future__ import annotations
 

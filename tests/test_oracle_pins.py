@@ -351,3 +351,93 @@ def test_varlen_sequences_are_independent():
     np.testing.assert_array_equal(S1[[0, 2]], S2[[0, 2]])
     np.testing.assert_array_equal(C1[[0, 1, 5]], C2[[0, 1, 5]])   # slots of sequences 0 and 2
     assert not np.allclose(o1[6:15], o2[6:15])
+
+
+# ---- layer prologue and epilogue ("Kimi K3: the manos...", section "Kimi
+#      Linear"; the log-decay bound of the trillion-scale page, section 4)
+
+from oracle import layer as OL
+
+
+def test_l2norm_against_torch_normalize():
+    x = np.random.default_rng(40).standard_normal((3, 5, 2, 16)) * 7.0
+    ref = torch.nn.functional.normalize(torch.from_numpy(x), dim=-1).numpy()
+    np.testing.assert_allclose(OL.l2norm_f64(x, 0.0), ref, rtol=1e-14, atol=1e-15)
+    # the eps sits under the square root: a zero row stays zero, a row with
+    # squared norm n is divided by sqrt(n + eps)
+    z = OL.l2norm_f64(np.zeros((1, 4)), 1e-6)
+    np.testing.assert_array_equal(z, 0.0)
+    r = OL.l2norm_f64(np.array([[3.0, 4.0]]), 11.0)
+    np.testing.assert_allclose(r, [[0.5, 4.0 / 6.0]], rtol=1e-15)
+
+
+def test_bounded_log_decay_values():
+    from scipy.special import expit
+    g = np.array([0.0, 10.0, -10.0, 1.5, -40.0])
+    la = OL.log_decay_f64(g, OL.GATE_BOUNDED, dk=1, bound=5.0)
+    assert la[0] == -2.5                                   # the midpoint of (-5, 0)
+    np.testing.assert_allclose(la, -5.0 * expit(g), rtol=1e-15)
+    assert np.all(la < 0) and np.all(la > -5.0)            # inside the open interval
+    assert np.all(np.diff(OL.log_decay_f64(np.linspace(-8, 8, 50), OL.GATE_BOUNDED, 1)) < 0)
+    np.testing.assert_allclose(OL.log_decay_f64(np.array([0.0]), OL.GATE_BOUNDED, 1, bound=3.0),
+                               [-1.5])
+
+
+def test_scalar_gate_is_gated_deltanet():
+    # GATE_SCALAR through the layer equals the Gated DeltaNet recurrence
+    # S_t = alpha_t (I - beta_t k k^T) S_{t-1} + beta_t k v^T written by hand
+    q, k, v, _, beta, S0 = rand_inputs(1, 25, 1, 6, 5, 41)
+    a = -np.random.default_rng(42).uniform(0.01, 0.8, (1, 25, 1))
+    o, S = OL.layer_prefill_f64(q, k, v, a, beta, S0, gate=OL.GATE_SCALAR)
+    St = S0[0, 0].copy()
+    for t in range(25):
+        kt = k[0, t, 0][:, None]
+        St = math.exp(a[0, t, 0]) * (np.eye(6) - beta[0, t, 0] * kt @ kt.T) @ St \
+            + beta[0, t, 0] * kt @ v[0, t, 0][None, :]
+        np.testing.assert_allclose(o[0, t, 0], St.T @ q[0, t, 0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S[0, 0], St, rtol=1e-12, atol=1e-14)
+
+
+def test_norm_gate_against_torch_rms_norm():
+    rng = np.random.default_rng(43)
+    o = rng.standard_normal((2, 3, 4, 16)) * 3.0
+    z = rng.standard_normal((2, 3, 4, 16))
+    w = 1.0 + 0.1 * rng.standard_normal(16)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(o), (16,), torch.from_numpy(w), 1e-6)
+    ref = ref.numpy() * torch.sigmoid(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(OL.norm_gate_f64(o, z, w, 1e-6), ref, rtol=1e-13, atol=1e-14)
+    # fully open gate, unit weight: unit RMS per token and head, scale-free
+    big = np.full_like(z, 50.0)
+    out = OL.norm_gate_f64(o, big, None, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(out ** 2, axis=-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(OL.norm_gate_f64(7.0 * o, big, None, 0.0), out, rtol=1e-13)
+    # a closed-half gate (z = 0) halves it
+    np.testing.assert_allclose(OL.norm_gate_f64(o, 0 * z, None, 0.0), 0.5 * out, rtol=1e-13)
+
+
+def test_layer_l2norm_equals_prenormalised_inputs():
+    # raw q, k through the layer equal pre-normalised q, k through the op;
+    # and scaling raw q, k per token changes nothing
+    q, k, v, la, beta, S0 = rand_inputs(1, 20, 2, 8, 6, 44, unit=False)
+    tq = torch.nn.functional.normalize(torch.from_numpy(q), dim=-1).numpy()
+    tk = torch.nn.functional.normalize(torch.from_numpy(k), dim=-1).numpy()
+    o1, S1 = OL.layer_prefill_f64(q, k, v, la, beta, S0, l2norm=True, l2_eps=0.0)
+    o2, S2 = oracle.prefill_f64(tq, tk, v, la, beta, S0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(S1, S2, rtol=1e-13, atol=1e-14)
+    s = np.random.default_rng(45).uniform(0.5, 9.0, (1, 20, 2, 1))
+    o3, _ = OL.layer_prefill_f64(s * q, s * k, v, la, beta, S0, l2norm=True, l2_eps=0.0)
+    np.testing.assert_allclose(o3, o1, rtol=1e-12, atol=1e-13)
+
+
+def test_layer_decode_is_one_layer_prefill_token():
+    q, k, v, _, beta, S0 = rand_inputs(2, 1, 3, 8, 8, 46, unit=False)
+    g = np.random.default_rng(47).standard_normal((2, 1, 3, 8)) - 3.0
+    z = np.random.default_rng(48).standard_normal((2, 1, 3, 8))
+    w = np.linspace(0.5, 1.5, 8)
+    kw = dict(l2norm=True, gate=OL.GATE_BOUNDED, z=z, w=w)
+    o1, S1 = OL.layer_prefill_f64(q, k, v, g, beta, S0, **kw)
+    kw["z"] = z[:, 0]
+    o2, S2 = OL.layer_decode_f64(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0, **kw)
+    np.testing.assert_allclose(o2, o1[:, 0], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(S2, S1, rtol=1e-14, atol=1e-15)

@@ -31,7 +31,7 @@ import torch
 __all__ = [
     "PrefillConfig", "DecodeConfig", "PREFILL_CONFIGS", "DECODE_CONFIGS",
     "prefill_inputs", "prefill_inputs_per_head", "decode_state", "decode_step_inputs",
-    "VarlenConfig", "VARLEN_CONFIGS", "varlen_lengths", "varlen_inputs",
+    "VarlenConfig", "VARLEN_CONFIGS", "varlen_lengths", "varlen_inputs", "layer_inputs",
 ]
 
 
@@ -240,4 +240,43 @@ def varlen_inputs(base: PrefillConfig, lengths, *, H: Optional[int] = None,
     for n in lengths:
         cu.append(cu[-1] + int(n))
     out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32)
+    return out
+
+
+def layer_inputs(cfg: PrefillConfig, *, B: Optional[int] = None, T: Optional[int] = None,
+                 H: Optional[int] = None, seed: Optional[int] = None, device="cpu",
+                 dtype: Optional[torch.dtype] = None, decode: bool = False) -> dict:
+    """Inputs of the layer form (weight-free prologue and epilogue around the
+    op), as the projections would hand them over: raw q, k ~ N(0, 1) (not
+    normalised), the decay gate pre-activation g ~ N(-5, 1.5) per key channel
+    (so -5 sigmoid(g) is mostly a mild decay, with a tail of strong ones), a
+    scalar per-head log-decay a = -U(lo, hi) of the config for the Gated
+    DeltaNet form, beta as the config draws it, the output gate
+    pre-activation z ~ N(0, 1) and an RMS-norm weight w = 1 + 0.1 N(0, 1)
+    (fp32, [dv]). q, k, v, g, z in `dtype`; a, beta, w fp32. decode=True drops
+    the T axis (T = 1)."""
+    B = cfg.B if B is None else B
+    T = 1 if decode else (cfg.T if T is None else T)
+    H = cfg.H if H is None else H
+    dtype = cfg.dtype if dtype is None else dtype
+    seed = (cfg.seed if seed is None else seed) + 9_000_000
+    g = _gen(seed, device)
+    dk, dv = cfg.dk, cfg.dv
+    shp = (B, T, H)
+    out = dict(
+        q=torch.randn(shp + (dk,), generator=g, device=device).to(dtype),
+        k=torch.randn(shp + (dk,), generator=g, device=device).to(dtype),
+        v=torch.randn(shp + (dv,), generator=g, device=device).to(dtype),
+        g=(torch.randn(shp + (dk,), generator=g, device=device) * 1.5 - 5.0).to(dtype),
+        a=-(0.001 + 0.099 * torch.rand(shp, generator=g, device=device)),
+        beta=torch.sigmoid(torch.randn(shp, generator=g, device=device)),
+        z=torch.randn(shp + (dv,), generator=g, device=device).to(dtype),
+        w=1.0 + 0.1 * torch.randn((dv,), generator=g, device=device),
+    )
+    out["S0"] = None
+    if cfg.s0_std > 0:
+        out["S0"] = cfg.s0_std * torch.randn((B, H, dk, dv), generator=g, device=device)
+    if decode:
+        for n in ("q", "k", "v", "g", "a", "beta", "z"):
+            out[n] = out[n][:, 0]
     return out

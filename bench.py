@@ -256,6 +256,78 @@ def bench_varlen(vc, reps=5):
     return out
 
 
+def _time_calls(call, reps, stream):
+    import torch
+    call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+
+
+def bench_layer(cfg, reps=20):
+    """The layer form on the prefill workload: raw q, k normalised in the
+    kernel, the bounded gate (bf16 pre-activation) or the per-head scalar gate,
+    and the output norm-gate epilogue; and a decode step in the layer form on
+    the decode configuration. Timed beside the plain op."""
+    import torch
+    import gated_delta_rule_22_amd as kda
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    x = W.layer_inputs(cfg, device=dev)
+    la = (-5.0 * torch.sigmoid(x["g"].float())).contiguous()
+    o = torch.empty_like(x["v"])
+    Sf = torch.empty((cfg.B, cfg.H, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
+    ws_bytes = kda.kda_prefill_workspace_size(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, cfg.dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    tok_heads = cfg.B * cfg.T * cfg.H
+    elt = 2
+    out = {"workload": cfg.describe()}
+    runs = {
+        "plain": (lambda: kda.kda_prefill_fwd(x["q"], x["k"], x["v"], la, x["beta"], x["S0"],
+                                              o=o, S_final=Sf, workspace=ws),
+                  elt * 4 * cfg.dk + 4 * cfg.dk + 4),
+        "bounded_l2_normgate": (lambda: kda.kda_prefill_layer(
+            x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], gate_mode=kda.KDA_GATE_BOUNDED,
+            l2norm=True, z=x["z"], w=x["w"], o=o, S_final=Sf, workspace=ws),
+            elt * 6 * cfg.dk + 4),
+        "scalar_gate_l2": (lambda: kda.kda_prefill_layer(
+            x["q"], x["k"], x["v"], x["a"], x["beta"], x["S0"], gate_mode=kda.KDA_GATE_SCALAR,
+            l2norm=True, o=o, S_final=Sf, workspace=ws),
+            elt * 4 * cfg.dk + 8),
+    }
+    for name, (call, per_tok) in runs.items():
+        us = _time_calls(call, reps, stream)
+        nbytes = tok_heads * per_tok + cfg.B * cfg.H * 4 * cfg.dk * cfg.dv * (
+            1 + (cfg.s0_std > 0))
+        out[name] = {"us_per_call": us, "tokens_per_s": cfg.B * cfg.T / (us * 1e-6),
+                     "algorithmic_bytes": nbytes,
+                     "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    # decode step, layer form (bounded gate, L2, norm-gate fused in the kernel)
+    dc = W.DECODE_CONFIGS["decode"]
+    import dataclasses
+    xd = W.layer_inputs(dataclasses.replace(cfg, dk=dc.dk, dv=dc.dv), B=dc.B, H=dc.H,
+                        decode=True, device=dev)
+    S = W.decode_state(dc, device=dev)
+    od = torch.empty_like(xd["v"])
+    lad = (-5.0 * torch.sigmoid(xd["g"].float())).contiguous()
+    us_plain = _time_calls(lambda: kda.kda_decode_step(xd["q"], xd["k"], xd["v"], lad, xd["beta"],
+                                                       S, o=od), reps, stream)
+    us_layer = _time_calls(lambda: kda.kda_decode_layer(
+        xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], S, gate_mode=kda.KDA_GATE_BOUNDED,
+        l2norm=True, z=xd["z"], w=xd["w"], o=od), reps, stream)
+    out["decode"] = {"workload": dc.describe().replace("1024 steps ", ""),
+                     "plain_us": us_plain, "bounded_l2_normgate_us": us_layer}
+    return out
+
+
 def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18, min_seconds=10.0):
     """fp64 oracle on the host cores over a bounded sample of the same
     workload: whole heads (one per thread) over the first tokens of the
@@ -298,6 +370,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a known traffic)")
@@ -403,6 +476,16 @@ def main():
         _log(f"[bench] varlen {vl['ckpt']['us_per_call']:.1f} us with checkpoints, "
              f"{vl['no_ckpt']['us_per_call']:.1f} us without")
         result["varlen"] = vl
+
+    if not args.no_layer:
+        _log("[bench] layer form (prologue + epilogue)")
+        ly = bench_layer(cfg)
+        _log("[bench] layer " + ", ".join(
+            f"{n} {ly[n]['us_per_call']:.1f} us" for n in ("plain", "bounded_l2_normgate",
+                                                          "scalar_gate_l2")) +
+             f"; decode plain {ly['decode']['plain_us']:.1f} us, layer "
+             f"{ly['decode']['bounded_l2_normgate_us']:.1f} us")
+        result["layer"] = ly
 
     if not args.no_cpu:
         _log("[bench] cpu oracle baseline")

@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "KDAError", "lib_path", "load_library", "kda_status_string",
     "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_prefill_varlen_workspace_size",
-    "kda_prefill_varlen", "kda_decode_step", "kda_decode_multi",
+    "kda_prefill_varlen", "kda_decode_step", "kda_decode_multi", "kda_prefill_layer",
+    "kda_decode_layer", "KDA_GATE_LOG", "KDA_GATE_BOUNDED", "KDA_GATE_SCALAR",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +27,15 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_LOG, KDA_GATE_BOUNDED, KDA_GATE_SCALAR = 0, 1, 2
+
+
+class _LayerOpts(ctypes.Structure):
+    # kda_layer_opts in include/kda.h
+    _fields_ = [("gate", ctypes.c_int), ("decay_bound", ctypes.c_float),
+                ("l2norm_qk", ctypes.c_int), ("l2_eps", ctypes.c_float),
+                ("out_gate", ctypes.c_void_p), ("out_weight", ctypes.c_void_p),
+                ("out_eps", ctypes.c_float)]
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 
 
@@ -61,6 +71,12 @@ def load_library():
     lib.kda_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, i, i,
                                        fp, i, i, vp, sz, vp]
     lib.kda_prefill_varlen.restype = i
+    lib.kda_prefill_layer.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                      ctypes.POINTER(_LayerOpts), vp, sz, vp]
+    lib.kda_prefill_layer.restype = i
+    lib.kda_decode_layer.argtypes = [vp, vp, vp, vp, fp, fp, vp, i, i, i, i, i,
+                                     ctypes.POINTER(_LayerOpts), vp]
+    lib.kda_decode_layer.restype = i
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, vp]
     lib.kda_decode_step.restype = i
     lib.kda_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, vp]
@@ -270,4 +286,109 @@ def kda_decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_decode_multi")
+    return o
+
+
+def _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps):
+    return _LayerOpts(int(gate_mode), float(decay_bound), int(bool(l2norm)), float(l2_eps),
+                      None if z is None else z.data_ptr(), None if w is None else w.data_ptr(),
+                      float(out_eps))
+
+
+def _check_layer_extra(gate, gate_mode, tok_shape, dk, dv, dt, dev, z, w):
+    if gate_mode == KDA_GATE_LOG:
+        _check(gate, "gate", tok_shape + (dk,), torch.float32, dev)
+    elif gate_mode == KDA_GATE_BOUNDED:
+        _check(gate, "gate", tok_shape + (dk,), dt, dev)
+    elif gate_mode == KDA_GATE_SCALAR:
+        _check(gate, "gate", tok_shape, torch.float32, dev)
+    else:
+        raise ValueError(f"unknown gate mode {gate_mode}")
+    if z is not None:
+        _check(z, "z", tok_shape + (dv,), dt, dev)
+    if w is not None:
+        _check(w, "w", (dv,), torch.float32, dev)
+
+
+def kda_prefill_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+                      beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
+                      gate_mode: int = KDA_GATE_LOG, decay_bound: float = 5.0,
+                      l2norm: bool = False, l2_eps: float = 1e-6,
+                      z: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                      out_eps: float = 1e-6, chunk: int = 64,
+                      o: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                      want_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill in the layer form: q, k raw or normalised ([B,T,H,dk]), gate
+    per gate_mode (fp32 log-decay [B,T,H,dk]; pre-activation g in the q dtype
+    [B,T,H,dk]; fp32 per-head log-decay [B,T,H]), optional epilogue with z
+    [B,T,H,dv] and w [dv]. Returns (o, S_final or None)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_prefill_layer needs GPU tensors")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    _check_layer_extra(gate, gate_mode, (B, T, H), dk, dv, dt, dev, z, w)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, T, H, dv), dt, dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    ws_bytes = kda_prefill_workspace_size(B, T, H, dk, dv, dt, chunk)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    opts = _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps)
+    st = lib.kda_prefill_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
+                               _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
+                               ctypes.byref(opts), _ptr(workspace), wsz, _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_layer")
+    return o, S_final
+
+
+def kda_decode_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+                     beta: torch.Tensor, S: torch.Tensor, *, gate_mode: int = KDA_GATE_LOG,
+                     decay_bound: float = 5.0, l2norm: bool = False, l2_eps: float = 1e-6,
+                     z: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                     out_eps: float = 1e-6, o: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """One decode step in the layer form (shapes as kda_decode_step, gate per
+    gate_mode: [B,H,dk] or [B,H]); S updated in place. Returns o [B,H,dv]."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_decode_layer needs GPU tensors")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (B, H, dk), dt, dev)
+    _check(k, "k", (B, H, dk), dt, dev)
+    _check(v, "v", (B, H, dv), dt, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, dk, dv), torch.float32, dev)
+    _check_layer_extra(gate, gate_mode, (B, H), dk, dv, dt, dev, z, w)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _check(o, "o", (B, H, dv), dt, dev)
+    opts = _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps)
+    st = lib.kda_decode_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
+                              _ptr(o), B, H, dk, dv, _DTYPES[dt], ctypes.byref(opts),
+                              _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_layer")
     return o

@@ -119,11 +119,11 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
         const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
         if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H, (int)nch,
-                                     ws, nullptr, 0, st);
+                                     ws, nullptr, 0, 0, kda::Prologue{}, st);
     } else {
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
                                         S_final, sq, H, dk, dv, chunk ? chunk : 64, nullptr, 0,
-                                        st);
+                                        0, kda::Prologue{}, st);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -210,11 +210,12 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
     if (dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H,
                                      (int)varlen_chunk_bound(N, T_total),
-                                     (char*)ws + varlen_table_bytes(N), S_ckpt, ckpt_slots, st);
+                                     (char*)ws + varlen_table_bytes(N), S_ckpt, ckpt_slots, 0,
+                                     kda::Prologue{}, st);
     else
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
                                         S_final, sq, H, dk, dv, chunk ? chunk : 64, S_ckpt,
-                                        ckpt_slots, st);
+                                        ckpt_slots, 0, kda::Prologue{}, st);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -243,8 +244,10 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
         if (overlap(ro, in) || overlap(rS, in)) return KDA_ERR_INVALID_ARG;
     if (overlap(ro, rS)) return KDA_ERR_INVALID_ARG;
 
-    const hipError_t e = kda::launch_decode(dtype == KDA_BF16, dk, dv, q, k, v, log_alpha,
-                                            beta, S, o, (int)bh, (hipStream_t)stream);
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.gate = log_alpha; a.beta = beta; a.S = S; a.o = o;
+    a.BH = (int)bh;
+    const hipError_t e = kda::launch_decode(dtype == KDA_BF16, dk, dv, a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -279,6 +282,153 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v,
     const hipError_t e = kda::launch_decode_multi(dtype == KDA_BF16, dk, dv, q, k, v, log_alpha,
                                                   beta, S, o, n_commit, (int)bh, H, T,
                                                   (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Layer form: the weight-free prologue and epilogue around the op.
+
+namespace {
+
+struct LayerCfg {
+    int pro = 0;                 // kGate* | kProL2
+    kda::Prologue pr{1e-6f, 5.f};
+    const void* z = nullptr;
+    const float* w = nullptr;
+    float out_eps = 1e-6f;
+};
+
+// Validates opts (NULL = the plain op) and fills cfg. The gate input of
+// each mode has its own element size and per-token count.
+kda_status layer_cfg(const kda_layer_opts* opts, LayerCfg& cfg) {
+    if (!opts) return KDA_OK;
+    if (opts->gate != KDA_GATE_LOG && opts->gate != KDA_GATE_BOUNDED &&
+        opts->gate != KDA_GATE_SCALAR)
+        return KDA_ERR_INVALID_ARG;
+    if (!(opts->decay_bound >= 0.f) || !(opts->l2_eps >= 0.f) || !(opts->out_eps >= 0.f))
+        return KDA_ERR_INVALID_ARG;   // negative or NaN
+    cfg.pro = (int)opts->gate | (opts->l2norm_qk ? kda::kProL2 : 0);
+    if (opts->decay_bound > 0.f) cfg.pr.bound = opts->decay_bound;
+    if (opts->l2_eps > 0.f) cfg.pr.l2_eps = opts->l2_eps;
+    cfg.z = opts->out_gate;
+    cfg.w = opts->out_weight;
+    if (opts->out_eps > 0.f) cfg.out_eps = opts->out_eps;
+    if (cfg.w && ((uintptr_t)cfg.w & 3u)) return KDA_ERR_INVALID_ARG;
+    if (cfg.z && !aligned16(cfg.z)) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+}  // namespace
+
+kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const void* gate,
+                             const float* beta, const float* S0, void* o, float* S_final,
+                             int B, int T, int H, int dk, int dv, kda_dtype dtype, int chunk,
+                             const kda_layer_opts* opts, void* ws, size_t ws_bytes,
+                             void* stream) {
+    LayerCfg cfg;
+    const kda_status ls = layer_cfg(opts, cfg);
+    if (ls != KDA_OK) return ls;
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return KDA_OK;
+
+    const size_t elt = dtype == KDA_BF16 ? 2 : 4;
+    size_t tok = 1;
+    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H))
+        return KDA_ERR_INVALID_ARG;
+    size_t nk = tok, nv = tok, ns = (size_t)B * (size_t)H;
+    if (!mul_ok(nk, (size_t)dk) || !mul_ok(nv, (size_t)dv) || !mul_ok(ns, (size_t)dk * dv))
+        return KDA_ERR_INVALID_ARG;
+    if (nk > (SIZE_MAX >> 3) || nv > (SIZE_MAX >> 3) || ns > (SIZE_MAX >> 3))
+        return KDA_ERR_INVALID_ARG;
+
+    if (T > 0 && (!q || !k || !v || !gate || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, gate, beta, S0, o, S_final};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk);
+    if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need)) return KDA_ERR_WORKSPACE;
+    if (ws_need > 0 && !aligned16(ws)) return KDA_ERR_INVALID_ARG;
+
+    const int gm = cfg.pro & 3;
+    const size_t gate_bytes = gm == KDA_GATE_SCALAR ? tok * 4 : nk * (gm == KDA_GATE_LOG ? 4 : elt);
+    const bool has_t = T > 0;
+    const Range rq(q, has_t ? nk * elt : 0), rk(k, has_t ? nk * elt : 0),
+        rv(v, has_t ? nv * elt : 0), rg(gate, has_t ? gate_bytes : 0),
+        rb(beta, has_t ? tok * 4 : 0), rs0(S0, S0 ? ns * 4 : 0),
+        rz(cfg.z, (has_t && cfg.z) ? nv * elt : 0), rw(cfg.w, cfg.w ? (size_t)dv * 4 : 0);
+    const Range ro(o, has_t ? nv * elt : 0), rsf(S_final, S_final ? ns * 4 : 0),
+        rws(ws, ws_need);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rs0, rz, rw};
+    const Range outputs[] = {ro, rsf, rws};
+    for (const Range& out : outputs)
+        for (const Range& in : inputs)
+            if (overlap(out, in)) {
+                // the only permitted overlap: S_final is exactly S0
+                if (&out == &outputs[1] && &in == &inputs[5] && rsf.lo == rs0.lo) continue;
+                return KDA_ERR_INVALID_ARG;
+            }
+    if (overlap(ro, rsf) || overlap(ro, rws) || overlap(rsf, rws)) return KDA_ERR_INVALID_ARG;
+
+    hipStream_t st = (hipStream_t)stream;
+    const kda::SeqLayout sq{nullptr, B, T, kChunk, 0};
+    hipError_t e;
+    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
+        const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
+        if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
+        e = kda::launch_prefill_mfma(q, k, v, gate, beta, S0, o, S_final, sq, H, (int)nch, ws,
+                                     nullptr, 0, cfg.pro, cfg.pr, st);
+    } else {
+        e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, gate, beta, S0, o, S_final,
+                                        sq, H, dk, dv, chunk ? chunk : 64, nullptr, 0, cfg.pro,
+                                        cfg.pr, st);
+    }
+    if (e == hipSuccess && cfg.z && T > 0)
+        e = kda::launch_norm_gate(dtype == KDA_BF16, o, cfg.z, cfg.w, cfg.out_eps, o, (long)tok,
+                                  dv, st);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_layer(const void* q, const void* k, const void* v, const void* gate,
+                            const float* beta, float* S, void* o, int B, int H, int dk, int dv,
+                            kda_dtype dtype, const kda_layer_opts* opts, void* stream) {
+    LayerCfg cfg;
+    const kda_status ls = layer_cfg(opts, cfg);
+    if (ls != KDA_OK) return ls;
+    if (B < 0 || H < 0) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !gate || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, gate, beta, S, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_INVALID_ARG;
+    const size_t elt = dtype == KDA_BF16 ? 2 : 4;
+    size_t bh = 1;
+    if (!mul_ok(bh, (size_t)B) || !mul_ok(bh, (size_t)H)) return KDA_ERR_INVALID_ARG;
+    if (bh > (size_t)INT32_MAX / 4) return KDA_ERR_INVALID_ARG;
+    const int gm = cfg.pro & 3;
+    const size_t nk = bh * dk, nv = bh * dv, ns = bh * dk * dv;
+    const size_t gate_bytes = gm == KDA_GATE_SCALAR ? bh * 4 : nk * (gm == KDA_GATE_LOG ? 4 : elt);
+    const Range rq(q, nk * elt), rk(k, nk * elt), rv(v, nv * elt), rg(gate, gate_bytes),
+        rb(beta, bh * 4), rS(S, ns * 4), ro(o, nv * elt), rz(cfg.z, cfg.z ? nv * elt : 0),
+        rw(cfg.w, cfg.w ? (size_t)dv * 4 : 0);
+    const Range ins[] = {rq, rk, rv, rg, rb, rz, rw};
+    for (const Range& in : ins)
+        if (overlap(ro, in) || overlap(rS, in)) return KDA_ERR_INVALID_ARG;
+    if (overlap(ro, rS)) return KDA_ERR_INVALID_ARG;
+
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.S = S; a.o = o;
+    a.BH = (int)bh;
+    a.layer = true;
+    a.pro = cfg.pro;
+    a.pr = cfg.pr;
+    a.z = cfg.z;
+    a.w = cfg.w;
+    a.out_eps = cfg.out_eps;
+    const hipError_t e = kda::launch_decode(dtype == KDA_BF16, dk, dv, a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -97,6 +97,50 @@ struct SeqLayout {
 // Natural exponential through the hardware exp2 (v_exp_f32).
 __device__ __forceinline__ float exp_e(float x) { return __expf(x); }
 
+// Weight-free prologue of the layer form ("Kimi K3: the manos...", section
+// "Kimi Linear"): where the per-channel log-decay comes from, and whether q
+// and k arrive raw and are L2-normalised here.
+//   kGateLog      log-decay given, fp32 [.., dk]
+//   kGateBounded  gate pre-activation g in the q/k dtype, [.., dk]:
+//                 log_alpha = -bound * sigmoid(g), inside (-bound, 0)
+//   kGateScalar   one fp32 log-decay per token and head, [..]: the Gated
+//                 DeltaNet gate, broadcast over the key channels
+// Kernels that take the prologue as a template argument encode it as
+// PRO = gate | (l2 ? 4 : 0); PRO = 0 is the plain op.
+enum : int { kGateLog = 0, kGateBounded = 1, kGateScalar = 2, kProL2 = 4 };
+struct Prologue {
+    float l2_eps;   // q_hat = q / sqrt(sum q^2 + l2_eps)
+    float bound;    // kGateBounded
+};
+
+// sigmoid through v_exp_f32 and v_rcp_f32 (about 1 ulp each)
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + exp_e(-x));
+}
+
+// One DPP move (dpp_ctrl CTRL, rows ROWS) of a float; lanes of rows outside
+// ROWS read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave as a wave-uniform value, without LDS:
+// DPP adds inside each 16-lane row (quad permutes [1,0,3,2] and [2,3,0,1],
+// then row rotates by 4 and 8 lanes leave the row sum in every lane), then
+// row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3 leave
+// the total in row 3, read from lane 63.
+__device__ __forceinline__ float wave_sum_uniform(float x) {
+    x += dpp_f<0xB1>(x);         // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);         // quad_perm [2,3,0,1]
+    x += dpp_f<0x124>(x);        // row_ror:4
+    x += dpp_f<0x128>(x);        // row_ror:8
+    x += dpp_f<0x142, 0xA>(x);   // row_bcast:15
+    x += dpp_f<0x143, 0xC>(x);   // row_bcast:31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // Workgroup barrier for LDS hazards only: waits for this wave's LDS (and
 // scalar) operations, not for outstanding global loads, so register
 // prefetches stay in flight across it.

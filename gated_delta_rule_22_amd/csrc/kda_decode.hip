@@ -45,11 +45,17 @@ __device__ __forceinline__ void load_row_vals(const T* __restrict__ p, float (&o
     }
 }
 
-template <int DK, int DV, typename T>
+// LAYER: the layer form. The log-decay comes from `gate` as `pro` says
+// (kGateLog / kGateBounded / kGateScalar), q and k are L2-normalised when
+// pro has kProL2, and when z is given the output leaves as
+// w * o / sqrt(mean(o^2) + out_eps) * sigmoid(z), the mean taken over the
+// head's DV columns (the waves of one head share a workgroup).
+template <int DK, int DV, typename T, bool LAYER>
 __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    float* __restrict__ S, T* __restrict__ o, int BH)
+    const void* __restrict__ gate, const float* __restrict__ beta,
+    float* __restrict__ S, T* __restrict__ o, int BH, int pro, Prologue pr,
+    const T* __restrict__ z, const float* __restrict__ ow, float out_eps)
 {
     constexpr int NC = DV < 32 ? DV : 32;   // columns per wave
     constexpr int NCG = NC / 4;             // float4 column groups
@@ -61,14 +67,17 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int head = gw / SLICES;
-    if (head >= BH) return;
+    // the layer epilogue reduces across the waves of a head: no early exit
+    if (!LAYER && head >= BH) return;
+    const bool live = head < BH;
+    const int hd = live ? head : BH - 1;    // idle waves re-read the last head
     const int slice = gw - head * SLICES;
     const int cg = lane % NCG;
     const int rg = lane / NCG;
     const int col = slice * NC + cg * 4;
     const int row0 = rg * RPL;
 
-    float* Sh = S + (size_t)head * DK * DV;
+    float* Sh = S + (size_t)hd * DK * DV;
     f32x4 s[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
@@ -76,17 +85,30 @@ __global__ __launch_bounds__(256) void decode_kernel(
             reinterpret_cast<const f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
 
     float kr[RPL], qr[RPL], lar[RPL];
-    load_row_vals<T, RPL>(k + (size_t)head * DK + row0, kr);
-    load_row_vals<T, RPL>(q + (size_t)head * DK + row0, qr);
-    load_row_vals<float, RPL>(log_alpha + (size_t)head * DK + row0, lar);
+    load_row_vals<T, RPL>(k + (size_t)hd * DK + row0, kr);
+    load_row_vals<T, RPL>(q + (size_t)hd * DK + row0, qr);
+    const int gm = LAYER ? (pro & 3) : kGateLog;
+    if (gm == kGateLog) {
+        load_row_vals<float, RPL>(static_cast<const float*>(gate) + (size_t)hd * DK + row0, lar);
+    } else if (gm == kGateBounded) {
+        load_row_vals<T, RPL>(static_cast<const T*>(gate) + (size_t)hd * DK + row0, lar);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) lar[r] = -pr.bound * sigmoid_f(lar[r]);
+    } else {
+        const float a = static_cast<const float*>(gate)[hd];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) lar[r] = a;
+    }
     float vv[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[(size_t)head * DV + col + c]);
-    const float b = beta[head];
+    for (int c = 0; c < 4; ++c) vv[c] = to_f32(v[(size_t)hd * DV + col + c]);
+    const float b = beta[hd];
 
     // Decay rows, then the two column reductions and k.q over this lane's rows.
+    // (With L2 normalisation the per-head factors of k and q are applied to
+    // the reduced sums: S^T k_hat = (S^T k) / |k|.)
     f32x4 w = zero4(), p = zero4();
-    float kq = 0.f;
+    float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const float a = exp_e(lar[r]);
@@ -94,6 +116,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
         w += s[r] * kr[r];
         p += s[r] * qr[r];
         kq += kr[r] * qr[r];
+        if (LAYER) {
+            kk += kr[r] * kr[r];
+            qq += qr[r] * qr[r];
+        }
     }
 #pragma unroll
     for (int off = NCG; off < kWave; off <<= 1) {
@@ -103,22 +129,62 @@ __global__ __launch_bounds__(256) void decode_kernel(
             p[c] += __shfl_xor(p[c], off);
         }
         kq += __shfl_xor(kq, off);
+        if (LAYER) {
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
+        }
+    }
+    if (LAYER && (pro & kProL2)) {
+        const float ks = __builtin_amdgcn_rsqf(kk + pr.l2_eps);
+        const float qs = __builtin_amdgcn_rsqf(qq + pr.l2_eps);
+        w *= ks;
+        p *= qs;
+        kq *= ks * qs;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) kr[r] *= ks;
     }
 
     f32x4 u;
 #pragma unroll
     for (int c = 0; c < 4; ++c) u[c] = b * (vv[c] - w[c]);
 
+    if (live) {
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        const f32x4 sn = s[r] + kr[r] * u;
-        __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+        for (int r = 0; r < RPL; ++r) {
+            const f32x4 sn = s[r] + kr[r] * u;
+            __builtin_nontemporal_store(sn, reinterpret_cast<f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+        }
     }
 
-    if (rg == 0) {
-        T* oh = o + (size_t)head * DV + col;
+    f32x4 ov;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) oh[c] = from_f32<T>(p[c] + u[c] * kq);
+    for (int c = 0; c < 4; ++c) ov[c] = p[c] + u[c] * kq;
+    if (LAYER && z != nullptr) {
+        // mean of o^2 over the head's columns: this wave's column groups
+        // (lanes 0 .. NCG-1 of every row group hold the same values), then
+        // the SLICES waves of the head through LDS
+        __shared__ float part[4];
+        float sq = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+        for (int off = 1; off < NCG; off <<= 1) sq += __shfl_xor(sq, off);
+        const int wv = threadIdx.x >> 6;
+        if (lane == 0) part[wv] = sq;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int j = 0; j < SLICES; ++j) tot += part[(wv / SLICES) * SLICES + j];
+        const float rs = __builtin_amdgcn_rsqf(tot / DV + out_eps);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float g = sigmoid_f(to_f32(z[(size_t)hd * DV + col + c]));
+            const float wc = ow ? ow[col + c] : 1.f;
+            ov[c] = wc * ov[c] * rs * g;
+        }
+    }
+    if (live && rg == 0) {
+        T* oh = o + (size_t)hd * DV + col;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) oh[c] = from_f32<T>(ov[c]);
     }
 }
 
@@ -210,25 +276,28 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
 }
 
 template <int DK, int DV, typename T>
-static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* la,
-                                  const float* beta, float* S, void* o, int BH, hipStream_t st)
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st)
 {
     constexpr int NC = DV < 32 ? DV : 32;
-    const long waves = (long)BH * (DV / NC);
+    const long waves = (long)a.BH * (DV / NC);
     const int threads = 256;
     const long blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), dim3((unsigned)blocks), dim3(threads), 0, st,
-                       (const T*)q, (const T*)k, (const T*)v, la, beta, S, (T*)o, BH);
+    if (a.layer)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, T, true>), dim3((unsigned)blocks), dim3(threads),
+                           0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.gate, a.beta,
+                           a.S, (T*)a.o, a.BH, a.pro, a.pr, (const T*)a.z, a.w, a.out_eps);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, T, false>), dim3((unsigned)blocks), dim3(threads),
+                           0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.gate, a.beta,
+                           a.S, (T*)a.o, a.BH, 0, a.pr, (const T*)nullptr, nullptr, 0.f);
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t dispatch_dv(int dk, int dv, const void* q, const void* k, const void* v,
-                              const float* la, const float* beta, float* S, void* o, int BH,
-                              hipStream_t st)
+static hipError_t dispatch_dv(int dk, int dv, const DecodeArgs& a, hipStream_t st)
 {
 #define KDA_DEC_CASE(DKV, DVV) \
-    if (dk == DKV && dv == DVV) return launch_decode_t<DKV, DVV, T>(q, k, v, la, beta, S, o, BH, st);
+    if (dk == DKV && dv == DVV) return launch_decode_t<DKV, DVV, T>(a, st);
     KDA_DEC_CASE(16, 16) KDA_DEC_CASE(16, 32) KDA_DEC_CASE(16, 64) KDA_DEC_CASE(16, 128)
     KDA_DEC_CASE(32, 16) KDA_DEC_CASE(32, 32) KDA_DEC_CASE(32, 64) KDA_DEC_CASE(32, 128)
     KDA_DEC_CASE(64, 16) KDA_DEC_CASE(64, 32) KDA_DEC_CASE(64, 64) KDA_DEC_CASE(64, 128)
@@ -277,12 +346,10 @@ hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, cons
     return dispatch_multi<float>(dk, dv, q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
 }
 
-hipError_t launch_decode(bool bf16_io, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* la, const float* beta, float* S,
-                         void* o, int BH, hipStream_t st)
+hipError_t launch_decode(bool bf16_io, int dk, int dv, const DecodeArgs& a, hipStream_t st)
 {
-    if (bf16_io) return dispatch_dv<bf16>(dk, dv, q, k, v, la, beta, S, o, BH, st);
-    return dispatch_dv<float>(dk, dv, q, k, v, la, beta, S, o, BH, st);
+    if (bf16_io) return dispatch_dv<bf16>(dk, dv, a, st);
+    return dispatch_dv<float>(dk, dv, a, st);
 }
 
 }  // namespace kda

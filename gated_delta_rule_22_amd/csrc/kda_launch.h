@@ -8,10 +8,22 @@
 
 namespace kda {
 
-// Decode step over B*H heads.
-hipError_t launch_decode(bool bf16_io, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* la, const float* beta, float* S,
-                         void* o, int BH, hipStream_t st);
+// Decode step over BH heads; layer = false is the plain op (gate = fp32
+// log-decay, pro and the epilogue fields unused).
+struct DecodeArgs {
+    const void *q, *k, *v, *gate;
+    const float* beta;
+    float* S;
+    void* o;
+    int BH;
+    bool layer;
+    int pro;              // kGate* | kProL2
+    Prologue pr;
+    const void* z;        // epilogue gate input [BH, dv] or null
+    const float* w;       // epilogue norm weight [dv] or null (ones)
+    float out_eps;
+};
+hipError_t launch_decode(bool bf16_io, int dk, int dv, const DecodeArgs& a, hipStream_t st);
 
 // Multi-token decode over B*H heads, T = ntok tokens each; S advanced by the
 // first n_commit[b] tokens (all when n_commit is null).
@@ -26,11 +38,13 @@ hipError_t launch_varlen_table(const int* cu, int N, int T, int C, int K, int* t
                                hipStream_t st);
 
 // Generic chunked prefill (fp32 arithmetic, any supported dk/dv/chunk, fp32 or
-// bf16 I/O) over the sequences of `sq`; checkpoints when S_ckpt and sq.K are set.
+// bf16 I/O) over the sequences of `sq`; checkpoints when S_ckpt and sq.K are
+// set; layer prologue `pro` (kGate* | kProL2, 0 = plain op).
 hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, const void* v,
-                                  const float* la, const float* beta, const float* S0,
+                                  const void* gate, const float* beta, const float* S0,
                                   void* o, float* S_final, const SeqLayout& sq, int H, int dk,
-                                  int dv, int chunk, float* S_ckpt, int ck_slots, hipStream_t st);
+                                  int dv, int chunk, float* S_ckpt, int ck_slots, int pro,
+                                  const Prologue& pr, hipStream_t st);
 
 // bf16 MFMA chunked prefill for dk = dv = 128, chunk 64, over the sequences
 // of `sq` (sq.C = 64). Below 128 sequence-heads it runs a chunk-parallel prep
@@ -40,9 +54,15 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
 bool prefill_mfma_supported(int dk, int dv, int chunk);
 bool prefill_mfma_split(long pairs);
 size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H);
-hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* gate,
                                const float* beta, const float* S0, void* o, float* S_final,
                                const SeqLayout& sq, int H, int nch_all, void* ws,
-                               float* S_ckpt, int ck_slots, hipStream_t st);
+                               float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
+                               hipStream_t st);
+
+// Layer epilogue over rows of dv values (one token and head each), in place
+// allowed: out = w * o / sqrt(mean(o^2) + eps) * sigmoid(z); w may be null.
+hipError_t launch_norm_gate(bool bf16_io, const void* o, const void* z, const float* w,
+                            float eps, void* out, long rows, int dv, hipStream_t st);
 
 }  // namespace kda

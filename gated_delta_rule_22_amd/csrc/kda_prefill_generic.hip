@@ -33,15 +33,16 @@ constexpr int kMaxD = 128;
 template <typename T>
 __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const void* __restrict__ gate, const float* __restrict__ beta,
     const float* S0, T* __restrict__ o, float* S_final,
-    SeqLayout sq, int H, int dk, int dv, int C, float* __restrict__ S_ckpt, int ck_slots)
+    SeqLayout sq, int H, int dk, int dv, int C, float* __restrict__ S_ckpt, int ck_slots,
+    int pro, Prologue pr)
 {
     __shared__ float sS[gen::kMaxD * gen::kMaxD];
     __shared__ float sQ[gen::kTile], sK[gen::kTile], sCum[gen::kTile], sKd[gen::kTile];
     __shared__ float sV[gen::kTile], sU[gen::kTile];
     __shared__ float sL[gen::kMaxC * gen::kMaxC], sM[gen::kMaxC * gen::kMaxC];
-    __shared__ float sBeta[gen::kMaxC], sAlast[gen::kMaxD];
+    __shared__ float sBeta[gen::kMaxC], sAlast[gen::kMaxD], sScale[2 * gen::kMaxC];
 
     const int tid = threadIdx.x;
     const int NT = blockDim.x;
@@ -61,12 +62,16 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
         // token-head row index of token t of this chunk
         auto row = [&](int t) -> size_t { return ((size_t)tok0 + c0 + t) * H + h; };
 
+        const int gm = pro & 3;
         for (int i = tid; i < n * dk; i += NT) {
             const int t = i / dk, d = i - t * dk;
             const size_t g = row(t) * dk + d;
             sQ[i] = to_f32(q[g]);
             sK[i] = to_f32(k[g]);
-            sCum[i] = log_alpha[g];
+            // log-decay from the gate input (plain op: given)
+            if (gm == kGateLog) sCum[i] = static_cast<const float*>(gate)[g];
+            else if (gm == kGateBounded) sCum[i] = -pr.bound / (1.f + expf(-to_f32(static_cast<const T*>(gate)[g])));
+            else sCum[i] = static_cast<const float*>(gate)[row(t)];
         }
         for (int i = tid; i < n * dv; i += NT) {
             const int t = i / dv, j = i - t * dv;
@@ -74,6 +79,23 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
         }
         for (int t = tid; t < n; t += NT) sBeta[t] = beta[row(t)];
         __syncthreads();
+
+        // layer prologue: q, k L2-normalised per token
+        if (pro & kProL2) {
+            for (int t = tid; t < 2 * n; t += NT) {
+                float* x = (t < n ? sQ : sK) + (t % n) * dk;
+                float ss = 0.f;
+                for (int d = 0; d < dk; ++d) ss += x[d] * x[d];
+                sScale[t] = 1.f / sqrtf(ss + pr.l2_eps);
+            }
+            __syncthreads();
+            for (int i = tid; i < n * dk; i += NT) {
+                const int t = i / dk;
+                sQ[i] *= sScale[t];
+                sK[i] *= sScale[n + t];
+            }
+            __syncthreads();
+        }
 
         // chunk-local inclusive cumulative log-decay, one channel per thread
         for (int d = tid; d < dk; d += NT) {
@@ -166,9 +188,10 @@ __global__ __launch_bounds__(gen::kThreads) void prefill_generic_kernel(
 }
 
 hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, const void* v,
-                                  const float* la, const float* beta, const float* S0,
+                                  const void* gate, const float* beta, const float* S0,
                                   void* o, float* S_final, const SeqLayout& sq, int H, int dk,
-                                  int dv, int chunk, float* S_ckpt, int ck_slots, hipStream_t st)
+                                  int dv, int chunk, float* S_ckpt, int ck_slots, int pro,
+                                  const Prologue& pr, hipStream_t st)
 {
     // Largest chunk whose tiles fit the LDS budget; the chunk length changes
     // only the blocking, never the result.
@@ -179,12 +202,12 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
     const dim3 grid((unsigned)((long)sq.N * H));
     if (bf16_io)
         hipLaunchKernelGGL(prefill_generic_kernel<bf16>, grid, dim3(gen::kThreads), 0, st,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S0,
-                           (bf16*)o, S_final, sq, H, dk, dv, C, S_ckpt, ck_slots);
+                           (const bf16*)q, (const bf16*)k, (const bf16*)v, gate, beta, S0,
+                           (bf16*)o, S_final, sq, H, dk, dv, C, S_ckpt, ck_slots, pro, pr);
     else
         hipLaunchKernelGGL(prefill_generic_kernel<float>, grid, dim3(gen::kThreads), 0, st,
-                           (const float*)q, (const float*)k, (const float*)v, la, beta, S0,
-                           (float*)o, S_final, sq, H, dk, dv, C, S_ckpt, ck_slots);
+                           (const float*)q, (const float*)k, (const float*)v, gate, beta, S0,
+                           (float*)o, S_final, sq, H, dk, dv, C, S_ckpt, ck_slots, pro, pr);
     return hipGetLastError();
 }
 

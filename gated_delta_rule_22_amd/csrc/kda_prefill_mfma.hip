@@ -80,6 +80,7 @@ struct Prep {
     float alast[DK];     // decay over the whole chunk
     float Tot[8 * DK];   // log-decay sums of the 8-or-4 token ranges
     float beta[C];
+    float qs[C], ks[C];  // layer prologue: per-token L2 factors of q and k
     int strong[8];       // per token range: some channel decays by more than kRangeDecay
 };
 
@@ -140,7 +141,8 @@ template <int NW>
 struct Inputs {
     static constexpr int TPT = C / NW;        // tokens per thread (16 or 8)
     uint32_t k[TPT], q[TPT];                  // two channels, bf16 pair
-    f32x2 la[TPT];                            // two channels' log-decay
+    f32x2 la[TPT];                            // two channels' log-decay (raw gate bits
+                                              // in .x for kGateBounded until converted)
     uint4 v[2];                               // two 16-byte pieces of the value block
     float beta;
 };
@@ -150,14 +152,15 @@ struct Inputs {
 // Loads are unconditional (tail tokens re-read the last token) and the raw
 // values are kept as loaded: tail tokens are zeroed where they are consumed,
 // so no instruction waits on a load before the next chunk is needed.
-template <int NW, int DVB>
+template <int NW, int DVB, int PRO>
 __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k,
                                             const bf16* __restrict__ v,
-                                            const float* __restrict__ log_alpha,
+                                            const void* __restrict__ gate,
                                             const float* __restrict__ beta, long tok0, int len,
                                             int h, int H, int c, int col0)
 {
+    constexpr int GM = PRO & 3;
     constexpr int TPT = C / NW;
     constexpr int VPR = DVB / 8;   // 16-byte pieces per value row
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -166,10 +169,19 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
     auto row = [&](int tok) -> size_t { return ((size_t)tok0 + min(tok, len - 1)) * H + h; };
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
-        const size_t base = row(c * C + t0 + j) * DK + 2 * lane;
+        const size_t rw = row(c * C + t0 + j);
+        const size_t base = rw * DK + 2 * lane;
         in.k[j] = *reinterpret_cast<const uint32_t*>(k + base);
         in.q[j] = *reinterpret_cast<const uint32_t*>(q + base);
-        in.la[j] = *reinterpret_cast<const f32x2*>(log_alpha + base);
+        if constexpr (GM == kGateLog) {
+            in.la[j] = *reinterpret_cast<const f32x2*>(static_cast<const float*>(gate) + base);
+        } else if constexpr (GM == kGateBounded) {
+            const uint32_t bits = *reinterpret_cast<const uint32_t*>(static_cast<const bf16*>(gate) + base);
+            in.la[j] = f32x2{__builtin_bit_cast(float, bits), 0.f};
+        } else {
+            const float a = static_cast<const float*>(gate)[rw];
+            in.la[j] = f32x2{a, a};
+        }
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -178,6 +190,45 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
         in.v[p] = *reinterpret_cast<const uint4*>(v + row(c * C + t) * 128 + col0 + 8 * c8);
     }
     if (tid < C) in.beta = beta[row(c * C + tid)];
+}
+
+// Layer prologue on a chunk's inputs, before stage 1a: the bounded gate's
+// log-decay -bound * sigmoid(g) in fp32, and with kProL2 the per-token
+// factors 1 / sqrt(|q|^2 + eps), 1 / sqrt(|k|^2 + eps) to LDS (stage 1b
+// scales q and k by them, so each operand is rounded to bf16 once).
+template <int NW, int PRO>
+__device__ __forceinline__ void prologue(Prep& sm, Inputs<NW>& in, const Prologue& pr) {
+    constexpr int TPT = C / NW;
+    if constexpr ((PRO & 3) == kGateBounded) {
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const f32x2 g = unpack2(__builtin_bit_cast(uint32_t, in.la[j][0]));
+            in.la[j] = f32x2{-pr.bound * sigmoid_f(g[0]), -pr.bound * sigmoid_f(g[1])};
+        }
+    }
+    if constexpr ((PRO & kProL2) != 0) {
+        // squared norms by packed bf16 dot products (v_dot2: no unpacked
+        // copies that could stay live until stage 1b), summed over the wave
+        // without LDS; lane 0 stores the factors of the range's tokens
+        const int lane = threadIdx.x & 63, wave = wave_id();
+        float fq[TPT], fk[TPT];
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const bf16x2 qq = __builtin_bit_cast(bf16x2, in.q[j]);
+            const bf16x2 kk = __builtin_bit_cast(bf16x2, in.k[j]);
+            fq[j] = __builtin_amdgcn_rsqf(
+                wave_sum_uniform(__builtin_amdgcn_fdot2_f32_bf16(qq, qq, 0.f, false)) + pr.l2_eps);
+            fk[j] = __builtin_amdgcn_rsqf(
+                wave_sum_uniform(__builtin_amdgcn_fdot2_f32_bf16(kk, kk, 0.f, false)) + pr.l2_eps);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < TPT; j += 4) {
+                *reinterpret_cast<f32x4*>(&sm.qs[wave * TPT + j]) = f32x4{fq[j], fq[j + 1], fq[j + 2], fq[j + 3]};
+                *reinterpret_cast<f32x4*>(&sm.ks[wave * TPT + j]) = f32x4{fk[j], fk[j + 1], fk[j + 2], fk[j + 3]};
+            }
+        }
+    }
 }
 
 // Stage 1a: per-range log-decay sums; values and beta to LDS. Tokens at or
@@ -219,7 +270,7 @@ __device__ __forceinline__ bool chunk_is_mild(const Prep& sm) {
 // Stage 1b: decay-scaled operands. Thread (range = wave, channels 2*lane, +1).
 // The decay reference is the chunk start when `fast`, else the start of the
 // token's 16-token block. FULL: every token of the chunk is real.
-template <int NW, bool FULL>
+template <int NW, bool FULL, int PRO>
 __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok, bool fast) {
     constexpr int TPT = C / NW;
     constexpr int SPB = NW / 4;      // token ranges per 16-token block
@@ -286,8 +337,12 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
         run = la * kLog2e + run;
         const f32x2 bt = {__builtin_amdgcn_exp2f(run[0]), __builtin_amdgcn_exp2f(run[1])};    // <= 1
         const f32x2 ib = {__builtin_amdgcn_exp2f(-run[0]), __builtin_amdgcn_exp2f(-run[1])};  // bounded above
-        const f32x2 kk = ok ? unpack2(in.k[j]) : f32x2{0.f, 0.f};
-        const f32x2 qq = ok ? unpack2(in.q[j]) : f32x2{0.f, 0.f};
+        f32x2 kk = ok ? unpack2(in.k[j]) : f32x2{0.f, 0.f};
+        f32x2 qq = ok ? unpack2(in.q[j]) : f32x2{0.f, 0.f};
+        if constexpr ((PRO & kProL2) != 0) {
+            kk *= sm.ks[t];
+            qq *= sm.qs[t];
+        }
         const f32x2 kd = kk * bt;
         const f32x2 ki = kk * ib;
         *reinterpret_cast<uint32_t*>(&sm.Kd[t * KS + d0]) = pack2(kd[0], kd[1]);
@@ -647,13 +702,13 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&Sacc)[8], 
 // Fused kernel: one workgroup per (sequence*head, value block of 16*NW
 // columns). With CKPT it also stores the state after every sq.K tokens of the
 // sequence to checkpoint slot sq.ckpt0(i) + j - 1 (slots >= ck_slots are
-// dropped).
-template <int NW, bool CKPT>
+// dropped). PRO selects the layer prologue (plain op: 0).
+template <int NW, bool CKPT, int PRO>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const void* __restrict__ gate, const float* __restrict__ beta,
     const float* S0, bf16* __restrict__ o, float* S_final, SeqLayout sq, int H, int NVB,
-    float* __restrict__ S_ckpt, int ck_slots)
+    float* __restrict__ S_ckpt, int ck_slots, Prologue pr)
 {
     using namespace mf;
     constexpr int DVB = NW * 16;
@@ -686,23 +741,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const int nchunks = (len + C - 1) / C;
     const int ck_every = CKPT ? sq.K / C : 1;   // chunks per checkpoint
     const long ck0 = CKPT ? sq.ckpt0(b) : 0;
-    if (nchunks > 0) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, tok0, len, h, H, 0, col0);
+    if (nchunks > 0) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, tok0, len, h, H, 0, col0);
 
     for (int c = 0; c < nchunks; ++c) {
         const int ntok = len - c * C;
         lds_barrier();
+        prologue<NW, PRO>(sm, in, pr);
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
         const bool fast = chunk_is_mild<NW>(sm);
-        if (ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
-        else stage1b<NW, false>(sm, in, ntok, fast);
+        if (ntok >= C) stage1b<NW, true, PRO>(sm, in, ntok, fast);
+        else stage1b<NW, false, PRO>(sm, in, ntok, fast);
         // next chunk's inputs; with 8 waves, waves 4-7 (lighter Gram work)
         // fetch after stage 2, so their fetches queue while the inverses finish
         const bool early_fetch = NW < 8 || wave < 4;
-        if (c + 1 < nchunks && early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, tok0, len, h, H, c + 1, col0);
+        if (c + 1 < nchunks && early_fetch) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, tok0, len, h, H, c + 1, col0);
         lds_barrier();
         stage2<NW>(sm, fast);
-        if (c + 1 < nchunks && !early_fetch) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, tok0, len, h, H, c + 1, col0);
+        if (c + 1 < nchunks && !early_fetch) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, tok0, len, h, H, c + 1, col0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
@@ -772,11 +828,11 @@ struct ChunkMap {
 // Prep kernel: chunks [gc0, gc0 + cpw) of the chunk numbering, head h;
 // writes the operand record of chunk gc at record h * nch_all + gc. kTable:
 // the sequences come from a device table (fewer than 128 of them).
-template <bool kTable>
+template <bool kTable, int PRO>
 __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    char* __restrict__ ws, SeqLayout sq, int H, int cpw, int nch_all)
+    const void* __restrict__ gate, const float* __restrict__ beta,
+    char* __restrict__ ws, SeqLayout sq, int H, int cpw, int nch_all, Prologue pr)
 {
     using namespace mf;
     constexpr int NW = 8, DVB = 128;
@@ -794,24 +850,25 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     ChunkPos p{0, 1, 0};
     if (gc0 < gc1) {
         p = map.at(gc0);
-        load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, p.tok0, p.len, h, H, p.c, 0);
+        load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, p.tok0, p.len, h, H, p.c, 0);
     }
     for (int gc = gc0; gc < gc1; ++gc) {
         const int ntok = p.len - p.c * C;
         const bool more = gc + 1 < gc1;
         const ChunkPos pn = more ? map.next(p, gc) : p;
         lds_barrier();
+        prologue<NW, PRO>(sm, in, pr);
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
         const bool fast = chunk_is_mild<NW>(sm);
-        if (ntok >= C) stage1b<NW, true>(sm, in, ntok, fast);
-        else stage1b<NW, false>(sm, in, ntok, fast);
+        if (ntok >= C) stage1b<NW, true, PRO>(sm, in, ntok, fast);
+        else stage1b<NW, false, PRO>(sm, in, ntok, fast);
         // next chunk's inputs: waves 0-3 now; waves 4-7 (lighter Gram work)
         // after stage 2, so their fetches queue while the inverses finish
-        if (more && wave < 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        if (more && wave < 4) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         stage2<NW>(sm, fast);
-        if (more && wave >= 4) load_inputs<NW, DVB>(in, q, k, v, log_alpha, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        if (more && wave >= 4) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
@@ -1127,10 +1184,23 @@ size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H) {
     return (size_t)H * nch_all * mf::REC_BYTES;
 }
 
-hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const float* la,
-                               const float* beta, const float* S0, void* o, float* S_final,
-                               const SeqLayout& sq, int H, int nch_all, void* ws,
-                               float* S_ckpt, int ck_slots, hipStream_t st)
+namespace {
+
+// Kernel instances by prologue: the plain op (with or without checkpoints)
+// and the six layer forms (gate mode x L2), without checkpoints.
+template <int NW, int PRO>
+auto fused_kernel_for(bool ck) {
+    if constexpr (PRO == 0)
+        return ck ? prefill_fused_kernel<NW, true, 0> : prefill_fused_kernel<NW, false, 0>;
+    else
+        return prefill_fused_kernel<NW, false, PRO>;
+}
+
+template <int PRO>
+hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const void* gate,
+                           const float* beta, const float* S0, void* o, float* S_final,
+                           const SeqLayout& sq, int H, int nch_all, void* ws, float* S_ckpt,
+                           int ck_slots, const Prologue& pr, hipStream_t st)
 {
     const long pairs = (long)sq.N * H;
     const bool ck = S_ckpt != nullptr && sq.K > 0 && ck_slots > 0;
@@ -1138,11 +1208,10 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
         const bool wide = pairs >= 256;   // one 8-wave workgroup per pair, else two of 4 waves
         const dim3 grid((unsigned)(wide ? pairs : pairs * 2)), block(wide ? 512 : 256);
         const int nvb = wide ? 1 : 2;
-        auto kern = wide ? (ck ? prefill_fused_kernel<8, true> : prefill_fused_kernel<8, false>)
-                         : (ck ? prefill_fused_kernel<4, true> : prefill_fused_kernel<4, false>);
+        auto kern = wide ? fused_kernel_for<8, PRO>(ck) : fused_kernel_for<4, PRO>(ck);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                           (const bf16*)v, la, beta, S0, (bf16*)o, S_final, sq, H, nvb, S_ckpt,
-                           ck_slots);
+                           (const bf16*)v, gate, beta, S0, (bf16*)o, S_final, sq, H, nvb,
+                           S_ckpt, ck_slots, pr);
         return hipGetLastError();
     }
     // few sequence-heads: chunk-parallel prep, then the state walk
@@ -1151,10 +1220,13 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
         int cpw = (int)((work + 255) / 256);          // about one workgroup per CU
         if (cpw < 1) cpw = 1;
         const long ngrp = (nch_all + cpw - 1) / cpw;
-        hipLaunchKernelGGL(sq.tab ? prefill_prep_kernel<true> : prefill_prep_kernel<false>,
-                           dim3((unsigned)(H * ngrp)), dim3(512), 0, st,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, (char*)ws,
-                           sq, H, cpw, nch_all);
+        // (the layer forms take fixed-length batches only: no table variant)
+        auto prep = prefill_prep_kernel<false, PRO>;
+        if constexpr (PRO == 0)
+            if (sq.tab) prep = prefill_prep_kernel<true, 0>;
+        hipLaunchKernelGGL(prep, dim3((unsigned)(H * ngrp)), dim3(512), 0, st, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, gate, beta, (char*)ws, sq, H, cpw,
+                           nch_all, pr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1167,6 +1239,30 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                        dim3((unsigned)(groups * 64)), dim3(threads), 0, st, (const char*)ws, S0,
                        (bf16*)o, S_final, sq, H, (int)pairs, nch_all, S_ckpt, ck_slots);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* gate,
+                               const float* beta, const float* S0, void* o, float* S_final,
+                               const SeqLayout& sq, int H, int nch_all, void* ws,
+                               float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
+                               hipStream_t st)
+{
+#define KDA_PRO_CASE(P)                                                                     \
+    case P:                                                                                 \
+        return launch_mfma_pro<P>(q, k, v, gate, beta, S0, o, S_final, sq, H, nch_all, ws,  \
+                                  S_ckpt, ck_slots, pr, st);
+    switch (pro) {
+        KDA_PRO_CASE(0)
+        KDA_PRO_CASE(kGateBounded)
+        KDA_PRO_CASE(kGateScalar)
+        KDA_PRO_CASE(kProL2)
+        KDA_PRO_CASE(kProL2 | kGateBounded)
+        KDA_PRO_CASE(kProL2 | kGateScalar)
+    }
+#undef KDA_PRO_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kda

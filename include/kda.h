@@ -176,6 +176,64 @@ kda_status kda_decode_multi(const void* q, const void* k, const void* v,
                             int B, int T, int H, int dk, int dv,
                             kda_dtype dtype, void* stream);
 
+/*
+ * Layer form: the weight-free operations around the op, fused into its
+ * kernels ("Kimi K3: the manos...", section "Kimi Linear": q and k are
+ * L2-normalised, the decay gate comes from a projection, and the output is
+ * normalised per head and scaled by an output gate; the trillion-scale
+ * architecture page, section 4: the log-decay is bounded to (-5, 0)). The
+ * projections themselves need trained weights and stay with the caller,
+ * who passes their outputs.
+ *
+ * Gate input by mode (`gate` argument of the layer calls):
+ *   KDA_GATE_LOG      fp32 natural log-decay [.., dk], as log_alpha above
+ *   KDA_GATE_BOUNDED  pre-activation g [.., dk] in `dtype`:
+ *                     log_alpha = -decay_bound * sigmoid(g), inside (-decay_bound, 0)
+ *   KDA_GATE_SCALAR   fp32 log-decay per token and head [..] (no dk axis),
+ *                     applied to every key channel: the Gated DeltaNet gate
+ */
+typedef enum {
+    KDA_GATE_LOG = 0,
+    KDA_GATE_BOUNDED = 1,
+    KDA_GATE_SCALAR = 2
+} kda_gate;
+
+typedef struct {
+    kda_gate gate;
+    float decay_bound;         /* KDA_GATE_BOUNDED; 0 selects 5 */
+    int l2norm_qk;             /* nonzero: q, k arrive raw and are divided by
+                                  sqrt(sum of squares + l2_eps) per token and head */
+    float l2_eps;              /* 0 selects 1e-6 */
+    const void* out_gate;      /* z [.., dv] in `dtype` (16-byte aligned), or NULL: no
+                                  epilogue. Otherwise o = w * o / sqrt(mean(o^2) + out_eps)
+                                  * sigmoid(z), the mean over each token-head's dv values */
+    const float* out_weight;   /* w [dv] fp32, or NULL for ones */
+    float out_eps;             /* 0 selects 1e-6 */
+} kda_layer_opts;
+
+/*
+ * kda_prefill_fwd in the layer form: the same layouts, workspace and rules,
+ * with `gate` in place of log_alpha (its layout follows opts->gate) and the
+ * prologue and epilogue of `opts` (NULL: the plain op). Negative bounds or
+ * eps values and unknown gate modes are rejected; z and w count as inputs
+ * for the overlap rules. With an epilogue, o is written once by the prefill
+ * and then rewritten in place.
+ */
+kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const void* gate,
+                             const float* beta, const float* S0, void* o, float* S_final,
+                             int B, int T, int H, int dk, int dv, kda_dtype dtype, int chunk,
+                             const kda_layer_opts* opts, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/*
+ * kda_decode_step in the layer form (gate as above, one token: [B,H,dk] or
+ * [B,H] for KDA_GATE_SCALAR; z [B,H,dv]). The prologue and the epilogue run
+ * inside the decode kernel: the state is still read once and written once.
+ */
+kda_status kda_decode_layer(const void* q, const void* k, const void* v, const void* gate,
+                            const float* beta, float* S, void* o, int B, int H, int dk, int dv,
+                            kda_dtype dtype, const kda_layer_opts* opts, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* kda_status_string(kda_status status);
 

@@ -32,6 +32,7 @@ def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert set(syms) == {"kda_prefill_workspace_size", "kda_prefill_fwd",
                          "kda_prefill_varlen_workspace_size", "kda_prefill_varlen",
+                         "kda_prefill_layer", "kda_decode_layer",
                          "kda_decode_step", "kda_decode_multi", "kda_status_string"}
     for s in syms:
         assert hasattr(lib, s), s
@@ -187,6 +188,38 @@ def test_varlen_rejects(lib):
     assert varlen(lib, Sf=P(5, 256)) == INVALID       # partial overlap with S0
     assert varlen(lib, N=0) == OK                     # nothing to do
     assert varlen(lib, H=0) == OK
+
+
+def layer_prefill(lib, opts=None, *, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S0=P(5),
+                  o=P(6), Sf=P(7), B=1, T=64, H=2, dk=128, dv=128, dt=1, ws=P(10)):
+    return lib.kda_prefill_layer(q, k, v, g, beta, S0, o, Sf, B, T, H, dk, dv, dt, 64,
+                                 None if opts is None else ctypes.byref(opts), ws, 1 << 30, None)
+
+
+def layer_decode(lib, opts=None, *, q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), S=P(5), o=P(6),
+                 B=2, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_decode_layer(q, k, v, g, beta, S, o, B, H, dk, dv, dt,
+                                None if opts is None else ctypes.byref(opts), None)
+
+
+def test_layer_rejects(lib):
+    Opts = kda._LayerOpts
+    assert ctypes.sizeof(Opts) == 40            # the C struct's layout
+    for call in (layer_prefill, layer_decode):
+        assert call(lib, Opts(gate=3)) == INVALID            # unknown gate mode
+        assert call(lib, Opts(decay_bound=-1.0)) == INVALID
+        assert call(lib, Opts(l2_eps=float("nan"))) == INVALID
+        assert call(lib, Opts(out_eps=-1e-3)) == INVALID
+        assert call(lib, Opts(out_gate=BASE + (8 << 30) + 8)) == INVALID      # z misaligned
+        assert call(lib, Opts(out_weight=BASE + (8 << 30) + 2)) == INVALID    # w misaligned
+        assert call(lib, Opts(out_gate=BASE + (6 << 30))) == INVALID          # z is o
+        assert call(lib, g=None) == INVALID
+        assert call(lib, dv=48) == UNSUPPORTED
+    assert layer_prefill(lib, Opts(out_weight=BASE + (7 << 30))) == INVALID    # w in S_final
+    assert layer_prefill(lib, o=P(3, 1024)) == INVALID       # o inside the gate input
+    assert layer_prefill(lib, B=0) == OK
+    assert layer_decode(lib, S=P(3, 256)) == INVALID         # S inside the gate input
+    assert layer_decode(lib, H=0) == OK
 
 
 def test_binding_rejects_cpu_tensors():

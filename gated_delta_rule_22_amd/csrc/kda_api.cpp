@@ -118,8 +118,10 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
     if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
         const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
         if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
+        bool epi_done;
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H, (int)nch,
-                                     ws, nullptr, 0, 0, kda::Prologue{}, st);
+                                     ws, nullptr, 0, 0, kda::Prologue{}, kda::Epilogue{},
+                                     &epi_done, st);
     } else {
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
                                         S_final, sq, H, dk, dv, chunk ? chunk : 64, nullptr, 0,
@@ -207,11 +209,12 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
     const kda::SeqLayout sq{tab, N, T_total, kChunk, ckpt_every};
     // With no tokens every sequence is empty and only S_final = S0 remains:
     // the generic kernel does that without touching a chunk record.
+    bool epi_done;
     if (dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H,
                                      (int)varlen_chunk_bound(N, T_total),
                                      (char*)ws + varlen_table_bytes(N), S_ckpt, ckpt_slots, 0,
-                                     kda::Prologue{}, st);
+                                     kda::Prologue{}, kda::Epilogue{}, &epi_done, st);
     else
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
                                         S_final, sq, H, dk, dv, chunk ? chunk : 64, S_ckpt,
@@ -374,17 +377,19 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
     hipStream_t st = (hipStream_t)stream;
     const kda::SeqLayout sq{nullptr, B, T, kChunk, 0};
     hipError_t e;
+    bool epi_done = false;
     if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
         const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
         if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
+        const kda::Epilogue ep{cfg.z, cfg.w, cfg.out_eps};
         e = kda::launch_prefill_mfma(q, k, v, gate, beta, S0, o, S_final, sq, H, (int)nch, ws,
-                                     nullptr, 0, cfg.pro, cfg.pr, st);
+                                     nullptr, 0, cfg.pro, cfg.pr, ep, &epi_done, st);
     } else {
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, gate, beta, S0, o, S_final,
                                         sq, H, dk, dv, chunk ? chunk : 64, nullptr, 0, cfg.pro,
                                         cfg.pr, st);
     }
-    if (e == hipSuccess && cfg.z && T > 0)
+    if (e == hipSuccess && cfg.z && T > 0 && !epi_done)
         e = kda::launch_norm_gate(dtype == KDA_BF16, o, cfg.z, cfg.w, cfg.out_eps, o, (long)tok,
                                   dv, st);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

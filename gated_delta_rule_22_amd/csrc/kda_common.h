@@ -126,16 +126,30 @@ __device__ __forceinline__ float dpp_f(float v) {
         0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
 }
 
+// Sum over each 16-lane row (lanes 16j .. 16j+15), left in every lane of the
+// row: quad permutes [1,0,3,2] and [2,3,0,1], then row rotates by 4 and 8.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x124>(x);
+    x += dpp_f<0x128>(x);
+    return x;
+}
+
+// Layer epilogue inputs: o = w * o / sqrt(mean(o^2) + eps) * sigmoid(z).
+struct Epilogue {
+    const void* z;    // [tokens, H, dv] in the output dtype
+    const float* w;   // [dv] or null (ones)
+    float eps;
+};
+
 // Sum over the 64 lanes of a wave as a wave-uniform value, without LDS:
 // DPP adds inside each 16-lane row (quad permutes [1,0,3,2] and [2,3,0,1],
 // then row rotates by 4 and 8 lanes leave the row sum in every lane), then
 // row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3 leave
 // the total in row 3, read from lane 63.
 __device__ __forceinline__ float wave_sum_uniform(float x) {
-    x += dpp_f<0xB1>(x);         // quad_perm [1,0,3,2]
-    x += dpp_f<0x4E>(x);         // quad_perm [2,3,0,1]
-    x += dpp_f<0x124>(x);        // row_ror:4
-    x += dpp_f<0x128>(x);        // row_ror:8
+    x = row_sum16(x);
     x += dpp_f<0x142, 0xA>(x);   // row_bcast:15
     x += dpp_f<0x143, 0xC>(x);   // row_bcast:31
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));

@@ -50,7 +50,9 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
 // of `sq` (sq.C = 64). Below 128 sequence-heads it runs a chunk-parallel prep
 // kernel and a state kernel that communicate through `ws`
 // (prefill_mfma_workspace() bytes for nch_all chunks in the numbering);
-// otherwise one fused kernel.
+// otherwise one fused kernel. With ep.z set, the 128-column fused kernel
+// applies the layer epilogue itself and *epi_done says so; otherwise the
+// caller runs launch_norm_gate afterwards.
 bool prefill_mfma_supported(int dk, int dv, int chunk);
 bool prefill_mfma_split(long pairs);
 size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H);
@@ -58,7 +60,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* S0, void* o, float* S_final,
                                const SeqLayout& sq, int H, int nch_all, void* ws,
                                float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
-                               hipStream_t st);
+                               const Epilogue& ep, bool* epi_done, hipStream_t st);
 
 // Layer epilogue over rows of dv values (one token and head each), in place
 // allowed: out = w * o / sqrt(mean(o^2) + eps) * sigmoid(z); w may be null.

@@ -687,6 +687,35 @@ __device__ __forceinline__ void store_o(const f32x4 (&O)[4], bf16* stage, bf16* 
     *reinterpret_cast<uint4*>(dst + 8) = hi;
 }
 
+// store_o for the layer epilogue: O (fp32, already normalised and weighted)
+// goes through an fp32 staging slot, and lane t multiplies token t's 16
+// values by sigmoid(z) (zv: its 16 gate values) before the one bf16 rounding.
+constexpr int OTSF = 20;  // fp32 staging row stride: 16-byte aligned rows
+__device__ __forceinline__ void store_o_gated(const f32x4 (&O)[4], float* stage, const uint4 (&zv)[2],
+                                              bf16* __restrict__ o, size_t row0, size_t rstride,
+                                              int col0, int ntok) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage[(16 * I + 4 * g + i) * OTSF + r] = O[I][i];
+    lds_fence_wave();
+    const int t = min(lane, ntok - 1);
+    const uint32_t zw[8] = {zv[0].x, zv[0].y, zv[0].z, zv[0].w, zv[1].x, zv[1].y, zv[1].z, zv[1].w};
+    uint32_t packed[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&stage[t * OTSF + 4 * p]);
+        const f32x2 za = unpack2(zw[2 * p]), zb = unpack2(zw[2 * p + 1]);
+        packed[2 * p] = pack2(x[0] * sigmoid_f(za[0]), x[1] * sigmoid_f(za[1]));
+        packed[2 * p + 1] = pack2(x[2] * sigmoid_f(zb[0]), x[3] * sigmoid_f(zb[1]));
+    }
+    bf16* dst = o + (row0 + (size_t)t * rstride) * 128 + col0;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
 }  // namespace mf
 
 // ---------------------------------------------------------------------------
@@ -702,14 +731,20 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&Sacc)[8], 
 // Fused kernel: one workgroup per (sequence*head, value block of 16*NW
 // columns). With CKPT it also stores the state after every sq.K tokens of the
 // sequence to checkpoint slot sq.ckpt0(i) + j - 1 (slots >= ck_slots are
-// dropped). PRO selects the layer prologue (plain op: 0).
-template <int NW, bool CKPT, int PRO>
+// dropped). PRO selects the layer prologue (plain op: 0). EPI (128-column
+// workgroups only, which hold a whole head's output row) applies the layer
+// epilogue before the output store: per token the sum of o^2 over the
+// row's columns is reduced inside each wave's 16 columns by DPP and across
+// the eight waves through LDS, and z, fetched at the chunk start in the
+// accumulator layout, gates the result.
+template <int NW, bool CKPT, int PRO, bool EPI = false>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const void* __restrict__ gate, const float* __restrict__ beta,
     const float* S0, bf16* __restrict__ o, float* S_final, SeqLayout sq, int H, int NVB,
-    float* __restrict__ S_ckpt, int ck_slots, Prologue pr)
+    float* __restrict__ S_ckpt, int ck_slots, Prologue pr, Epilogue ep)
 {
+    static_assert(!EPI || NW == 8, "the fused epilogue needs the whole row in one workgroup");
     using namespace mf;
     constexpr int DVB = NW * 16;
     __shared__ Prep sm;
@@ -742,6 +777,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     const int ck_every = CKPT ? sq.K / C : 1;   // chunks per checkpoint
     const long ck0 = CKPT ? sq.ckpt0(b) : 0;
     if (nchunks > 0) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, tok0, len, h, H, 0, col0);
+    const float epi_w = (EPI && ep.w) ? ep.w[ncol] : 1.f;
 
     for (int c = 0; c < nchunks; ++c) {
         const int ntok = len - c * C;
@@ -763,11 +799,52 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
         lds_barrier();
+        // epilogue gate of this chunk in the output store's layout (lane t:
+        // token t, this wave's 16 columns), fetched while the state pass runs
+        uint4 zv[2];
+        if constexpr (EPI) {
+            const int t = min(lane, ntok - 1);
+            const bf16* zp = static_cast<const bf16*>(ep.z) +
+                             (((size_t)tok0 + (size_t)c * C + t) * H + h) * 128 + 16 * wave;
+            zv[0] = *reinterpret_cast<const uint4*>(zp);
+            zv[1] = *reinterpret_cast<const uint4*>(zp + 8);
+        }
         f32x4 O[4];
         state_pass<(NW < 8)>(Sacc, U0, sm.NWop, sm.Qd, sm.Mop, sm.KrT, sm.alast, O);
-        // staging slots: waves 0-4 in Kd, 5-7 in Ki (both dead until the next chunk)
-        bf16* stage = (wave < 5) ? sm.Kd + wave * (C * OTS) : sm.Ki + (wave - 5) * (C * OTS);
-        store_o(O, stage, o, ((size_t)tok0 + (size_t)c * C) * H + h, (size_t)H, col0 + 16 * wave, ntok);
+        if constexpr (EPI) {
+            __shared__ f32x4 epi_part[NW][C / 4];   // per wave: sum of o^2 over its 16 columns
+            float s2[4][4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s2[I][i] = row_sum16(O[I][i] * O[I][i]);
+            if (r == 0)
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+                    epi_part[wave][4 * I + g] = f32x4{s2[I][0], s2[I][1], s2[I][2], s2[I][3]};
+            lds_barrier();
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                f32x4 tot = epi_part[0][4 * I + g];
+#pragma unroll
+                for (int w2 = 1; w2 < NW; ++w2) tot += epi_part[w2][4 * I + g];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    O[I][i] *= __builtin_amdgcn_rsqf(tot[i] * (1.f / 128) + ep.eps) * epi_w;
+            }
+            // fp32 staging (slots of 64 x OTSF floats: waves 0-2 in Kd, 3-5 in
+            // Ki, 6-7 in RkT, all dead until the next chunk), so o is rounded
+            // to bf16 once, after the gate
+            float* stf = wave < 3 ? reinterpret_cast<float*>(sm.Kd) + wave * (C * OTSF)
+                       : wave < 6 ? reinterpret_cast<float*>(sm.Ki) + (wave - 3) * (C * OTSF)
+                                  : reinterpret_cast<float*>(sm.RkT) + (wave - 6) * (C * OTSF);
+            store_o_gated(O, stf, zv, o, ((size_t)tok0 + (size_t)c * C) * H + h, (size_t)H,
+                          16 * wave, ntok);
+        } else {
+            // staging slots: waves 0-4 in Kd, 5-7 in Ki (both dead until the next chunk)
+            bf16* stage = (wave < 5) ? sm.Kd + wave * (C * OTS) : sm.Ki + (wave - 5) * (C * OTS);
+            store_o(O, stage, o, ((size_t)tok0 + (size_t)c * C) * H + h, (size_t)H, col0 + 16 * wave, ntok);
+        }
         if (CKPT && ntok >= C && (c + 1) % ck_every == 0) {
             const long slot = ck0 + (c + 1) / ck_every - 1;
             if (slot < ck_slots) store_state(S_ckpt + ((size_t)slot * H + h) * DK * 128, Sacc, g, ncol);
@@ -1189,7 +1266,10 @@ namespace {
 // Kernel instances by prologue: the plain op (with or without checkpoints)
 // and the six layer forms (gate mode x L2), without checkpoints.
 template <int NW, int PRO>
-auto fused_kernel_for(bool ck) {
+auto fused_kernel_for(bool ck, bool epi) {
+    if constexpr (NW == 8) {
+        if (epi) return prefill_fused_kernel<8, false, PRO, true>;
+    }
     if constexpr (PRO == 0)
         return ck ? prefill_fused_kernel<NW, true, 0> : prefill_fused_kernel<NW, false, 0>;
     else
@@ -1200,18 +1280,22 @@ template <int PRO>
 hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const void* gate,
                            const float* beta, const float* S0, void* o, float* S_final,
                            const SeqLayout& sq, int H, int nch_all, void* ws, float* S_ckpt,
-                           int ck_slots, const Prologue& pr, hipStream_t st)
+                           int ck_slots, const Prologue& pr, const Epilogue& ep,
+                           bool* epi_done, hipStream_t st)
 {
     const long pairs = (long)sq.N * H;
     const bool ck = S_ckpt != nullptr && sq.K > 0 && ck_slots > 0;
+    *epi_done = false;
     if (!prefill_mfma_split(pairs)) {
         const bool wide = pairs >= 256;   // one 8-wave workgroup per pair, else two of 4 waves
         const dim3 grid((unsigned)(wide ? pairs : pairs * 2)), block(wide ? 512 : 256);
         const int nvb = wide ? 1 : 2;
-        auto kern = wide ? fused_kernel_for<8, PRO>(ck) : fused_kernel_for<4, PRO>(ck);
+        const bool epi = wide && ep.z != nullptr;
+        auto kern = wide ? fused_kernel_for<8, PRO>(ck, epi) : fused_kernel_for<4, PRO>(ck, false);
         hipLaunchKernelGGL(kern, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
                            (const bf16*)v, gate, beta, S0, (bf16*)o, S_final, sq, H, nvb,
-                           S_ckpt, ck_slots, pr);
+                           S_ckpt, ck_slots, pr, ep);
+        *epi_done = epi;
         return hipGetLastError();
     }
     // few sequence-heads: chunk-parallel prep, then the state walk
@@ -1247,12 +1331,12 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* S0, void* o, float* S_final,
                                const SeqLayout& sq, int H, int nch_all, void* ws,
                                float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
-                               hipStream_t st)
+                               const Epilogue& ep, bool* epi_done, hipStream_t st)
 {
 #define KDA_PRO_CASE(P)                                                                     \
     case P:                                                                                 \
         return launch_mfma_pro<P>(q, k, v, gate, beta, S0, o, S_final, sq, H, nch_all, ws,  \
-                                  S_ckpt, ck_slots, pr, st);
+                                  S_ckpt, ck_slots, pr, ep, epi_done, st);
     switch (pro) {
         KDA_PRO_CASE(0)
         KDA_PRO_CASE(kGateBounded)

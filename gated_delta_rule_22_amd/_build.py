@@ -20,7 +20,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill_generic.hip", "kda_prefill_mfma.hip",
-           "kda_varlen.hip", "kda_epilogue.hip"]
+           "kda_varlen.hip", "kda_epilogue.hip", "kda_decode_multi_mfma.hip"]
 
 
 def _compile(src: str) -> str:

@@ -342,6 +342,9 @@ hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, cons
                                void* o, const int* n_commit, int BH, int H, int ntok,
                                hipStream_t st)
 {
+    // drafts of 2..8 tokens in bf16 at d = 128 run on the matrix cores
+    if (decode_multi_mfma_supported(bf16_io, dk, dv, ntok))
+        return launch_decode_multi_mfma(q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
     if (bf16_io) return dispatch_multi<bf16>(dk, dv, q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
     return dispatch_multi<float>(dk, dv, q, k, v, la, beta, S, o, n_commit, BH, H, ntok, st);
 }

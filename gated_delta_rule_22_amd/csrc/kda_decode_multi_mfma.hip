@@ -1,0 +1,271 @@
+// Multi-token decode on the matrix cores: a draft of 2..8 tokens verified
+// (and an accepted prefix committed) from a live fp32 state, bf16 q/k/v,
+// dk = dv = 128.
+//
+// The T tokens form one small chunk of the chunk algebra ("Kimi K3: the
+// manos...", section "FlashKDA Algorithm"), with a_t the inclusive cumulative
+// decay from the draft start:
+//   W = [K_decay; Q_decay] S                (one 16-row MFMA tile: T <= 8 rows each)
+//   (I + L) U = Diag(beta)(V - K_decay S),  L_ts = beta_t sum_d k_t[d] (a_t/a_s)[d] k_s[d], s < t
+//   O = Q_decay S + M U,                    M_ts = sum_d q_t[d] (a_t/a_s)[d] k_s[d],       s <= t
+//   S_n = Diag(a_{n-1}) S + sum_{t<n} Diag(a_{n-1}/a_t) k_t u_t^T   (the accepted prefix n)
+// One workgroup per head, four waves, wave w owning value columns 32w..32w+31.
+// The state streams through the W product in MFMA accumulator layout (lane
+// (g, r) of a 16x16 tile: rows 4g..4g+3, column r), used directly as the B
+// operand with the K index of each 32-deep step permuted the same way on
+// both operands, so no state tile is held for long. The commit reads each
+// 16-row tile again (from the last-level cache, as a rule), adds
+// K_restore^T U to it in fp32 on the matrix cores and writes it back once;
+// a verify pass (n = 0) only reads the state.
+// With T <= 8 and the log-decay bound of (-5, 0) per step, 1/a_t <= e^40 stays
+// inside fp32.
+#include <type_traits>
+
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;
+constexpr int TM = 8;             // most draft tokens
+constexpr int AS = D + 8;         // bf16 row stride of [16][D] operand tiles
+constexpr int RS = 16 + 8;        // bf16 row stride of K_restore^T [D][16 token slots]
+
+// Buffer resource word 3 for raw 32-bit accesses on CDNA, and the cache
+// policy bit of a streaming (non-temporal) access. The b32 buffer builtins
+// move raw bits (uint32): floats go through bit casts.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kNT = 2;
+
+__device__ __forceinline__ bf16x8 ldA_perm8(const bf16* rowp, int k0, int g) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(rowp + k0 + 4 * g);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(rowp + k0 + 16 + 4 * g);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__global__ __launch_bounds__(256) void decode_multi_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    float* __restrict__ S, bf16* __restrict__ o, const int* __restrict__ n_commit,
+    int H, int T)
+{
+    // (16-byte aligned: operand rows are read as 8- and 16-byte vectors)
+#define KDA_LDS __shared__ __attribute__((aligned(16)))
+    KDA_LDS bf16 sA[16 * AS];      // rows 0..7: K_decay_t, rows 8..15: Q_decay_t (zero past T)
+    KDA_LDS bf16 sKrT[D * RS];     // K_restore^T [channel][token slot], zero for slots >= n
+    KDA_LDS bf16 sU[16 * AS];      // U (bf16) [token slot][column], zero for slots >= T
+    KDA_LDS float sKd[TM * D];
+    KDA_LDS float sQd[TM * D];
+    KDA_LDS float sKi[TM * D];
+    KDA_LDS float sW[16 * D];      // [K_decay; Q_decay] S
+    KDA_LDS float sL[TM * TM];
+    KDA_LDS float sM[TM * TM];
+    KDA_LDS float sDal[D];
+    KDA_LDS float sBeta[TM];
+#undef KDA_LDS
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int g = lane >> 4, r = lane & 15;
+    const int head = blockIdx.x;
+    const int bb = head / H, hh = head - bb * H;
+    int n = n_commit ? n_commit[bb] : T;
+    n = __builtin_amdgcn_readfirstlane(min(max(n, 0), T));
+
+    // ---- state slice, accumulator layout: Sa[m][ct] = rows 16m + 4g + i, column c0 + 16ct + r
+    // (buffer loads: a per-head resource, eight per-lane byte offsets and a
+    // uniform offset per 16-row block, so no per-element 64-bit address
+    // stays live until the store; nt = streaming, as in the decode step)
+    float* Sh = S + (size_t)head * D * D;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(Sh, 0, D * D * 4, kBufWord3);
+    const int c0 = 32 * wave;
+    int off[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) off[ct][i] = ((4 * g + i) * D + c0 + 16 * ct + r) * 4;
+    // ---- token side: one thread per channel d; threads 0-127 the key side
+    //      (k, and the value column d), 128-255 the query side. All token
+    //      loads are issued before any of them is used.
+    const int d = tid & (D - 1);
+    const bool kside = tid < D;
+    auto row = [&](int t) -> size_t { return ((size_t)bb * T + t) * H + hh; };
+    const bf16* kq = kside ? k : q;
+    float la_t[TM], x_t[TM], vcol[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        const int tt = min(t, T - 1);   // past T: re-read the last token, masked below
+        la_t[t] = log_alpha[row(tt) * D + d];
+        x_t[t] = (float)kq[row(tt) * D + d];
+        vcol[t] = kside ? (float)v[row(tt) * D + d] : 0.f;
+    }
+    const float beta_d = d < TM ? beta[row(min(d, T - 1))] : 0.f;
+    {
+        float c = 0.f, cn = 0.f;
+        float cum[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            if (t < T) c += la_t[t];
+            cum[t] = c;
+            if (t + 1 == n) cn = c;
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const float xt = t < T ? x_t[t] : 0.f;
+            const float xd = xt * exp_e(cum[t]);
+            if (kside) {
+                sKd[t * D + d] = xd;
+                sKi[t * D + d] = xt * exp_e(-cum[t]);
+                sA[t * AS + d] = (bf16)xd;
+                sKrT[d * RS + t] = (bf16)(t < n ? xt * exp_e(cn - cum[t]) : 0.f);
+                sKrT[d * RS + 8 + t] = (bf16)0.f;
+            } else {
+                sQd[t * D + d] = xd;
+                sA[(8 + t) * AS + d] = (bf16)xd;
+            }
+        }
+        if (kside) sDal[d] = exp_e(cn);
+        else if (d < TM) sBeta[d] = d < T ? beta_d : 0.f;
+    }
+    __syncthreads();
+
+    // ---- L and M: the 8 x 8 dot products over the channels, all at once:
+    //      thread (pair p = tid / 4, quarter j = tid % 4) sums channels
+    //      32j .. 32j + 31 of k_t.Ki_s and q_t.Ki_s, then a quad reduction
+    {
+        const int p = tid >> 2, j = tid & 3;
+        const int t = p >> 3, s = p & 7;
+        const f32x4* kd4 = reinterpret_cast<const f32x4*>(sKd + t * D + 32 * j);
+        const f32x4* qd4 = reinterpret_cast<const f32x4*>(sQd + t * D + 32 * j);
+        const f32x4* ki4 = reinterpret_cast<const f32x4*>(sKi + s * D + 32 * j);
+        f32x4 ak = zero4(), aq = zero4();
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const f32x4 ki = ki4[c];
+            ak += kd4[c] * ki;
+            aq += qd4[c] * ki;
+        }
+        float dk = ak[0] + ak[1] + ak[2] + ak[3];
+        float dq = aq[0] + aq[1] + aq[2] + aq[3];
+        dk += dpp_f<0xB1>(dk);   // quad_perm [1,0,3,2]
+        dq += dpp_f<0xB1>(dq);
+        dk += dpp_f<0x4E>(dk);   // quad_perm [2,3,0,1]
+        dq += dpp_f<0x4E>(dq);
+        if (j == 0) {
+            const bool live = t < T && s < T;
+            sL[p] = (live && s < t) ? sBeta[t] * dk : 0.f;
+            sM[p] = (live && s <= t) ? dq : 0.f;
+        }
+    }
+
+    // ---- W = [K_decay; Q_decay] S on the matrix cores, the state streaming
+    //      through one 32-row step at a time (rows 32kk + 4g + i and
+    //      32kk + 16 + 4g + i of this lane's column: the B operand as loaded)
+    // (streaming loads for a verify pass; cached ones when the commit will
+    // read the same tiles again)
+    f32x4 Wc[2] = {zero4(), zero4()};
+    auto w_pass = [&](auto aux) {
+        constexpr int kAux = decltype(aux)::value;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 a = ldA_perm8(sA + r * AS, 32 * kk, g);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 lo, hi;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off[ct][i], 32 * kk * D * 4, kAux));
+                    hi[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off[ct][i], (32 * kk + 16) * D * 4, kAux));
+                }
+                Wc[ct] = mma32(a, pack8(lo, hi), Wc[ct]);
+            }
+        }
+    };
+    if (n == 0) w_pass(std::integral_constant<int, kNT>{});
+    else w_pass(std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sW[(4 * g + i) * D + c0 + 16 * ct + r] = Wc[ct][i];
+    __syncthreads();
+
+    // ---- U by forward substitution and O, one value column per key-side thread
+    if (kside) {
+        float u[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            float x = 0.f;
+            if (t < T) {
+                x = sBeta[t] * (vcol[t] - sW[t * D + d]);
+#pragma unroll
+                for (int s = 0; s < t; ++s) x -= sL[t * TM + s] * u[s];
+            }
+            u[t] = x;
+            sU[t * AS + d] = (bf16)x;
+            sU[(8 + t) * AS + d] = (bf16)0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            if (t < T) {
+                float y = sW[(8 + t) * D + d];
+#pragma unroll
+                for (int s = 0; s <= t; ++s) y += sM[t * TM + s] * u[s];
+                o[row(t) * D + d] = (bf16)y;
+            }
+        }
+    }
+
+    // ---- commit the accepted prefix: S = Diag(a_{n-1}) S + K_restore^T U,
+    //      one 16-row tile at a time: the tile is read again (recently
+    //      streamed, so mostly from the last-level cache), decayed, updated on
+    //      the matrix cores in fp32 and written back
+    if (n == 0) return;   // verify pass: the state is only read (uniform)
+    __syncthreads();
+    // (the whole vector is bit-cast, then indexed: a bit cast of one vector
+    // element has been seen to lose the element index here)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    s16x4 b[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[ct][i] = __builtin_bit_cast(short, sU[(4 * g + i) * AS + c0 + 16 * ct + r]);
+    // all sixteen tiles' reloads first, so they are in flight together
+    f32x4 st[8][2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st[m][ct][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off[ct][i], 16 * m * D * 4, 0));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const f32x4 dal = *reinterpret_cast<const f32x4*>(&sDal[16 * m + 4 * g]);
+        const s16x4 a = *reinterpret_cast<const s16x4*>(&sKrT[(16 * m + r) * RS + 4 * g]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const u32x4 bits = __builtin_bit_cast(u32x4, mma16(a, b[ct], st[m][ct] * dal));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(bits[i], srs, off[ct][i], 16 * m * D * 4, 0);
+        }
+    }
+}
+
+}  // namespace
+
+bool decode_multi_mfma_supported(bool bf16_io, int dk, int dv, int ntok) {
+    return bf16_io && dk == D && dv == D && ntok >= 2 && ntok <= TM;
+}
+
+hipError_t launch_decode_multi_mfma(const void* q, const void* k, const void* v, const float* la,
+                                    const float* beta, float* S, void* o, const int* n_commit,
+                                    int BH, int H, int ntok, hipStream_t st)
+{
+    hipLaunchKernelGGL(decode_multi_mfma_kernel, dim3((unsigned)BH), dim3(256), 0, st,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, la, beta, S, (bf16*)o,
+                       n_commit, H, ntok);
+    return hipGetLastError();
+}
+
+}  // namespace kda

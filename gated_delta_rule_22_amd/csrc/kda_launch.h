@@ -37,6 +37,12 @@ hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, cons
 hipError_t launch_varlen_table(const int* cu, int N, int T, int C, int K, int* tab,
                                hipStream_t st);
 
+// Multi-token decode on the matrix cores (bf16, dk = dv = 128, 2 <= ntok <= 8).
+bool decode_multi_mfma_supported(bool bf16_io, int dk, int dv, int ntok);
+hipError_t launch_decode_multi_mfma(const void* q, const void* k, const void* v, const float* la,
+                                    const float* beta, float* S, void* o, const int* n_commit,
+                                    int BH, int H, int ntok, hipStream_t st);
+
 // Generic chunked prefill (fp32 arithmetic, any supported dk/dv/chunk, fp32 or
 // bf16 I/O) over the sequences of `sq`; checkpoints when S_ckpt and sq.K are
 // set; layer prologue `pro` (kGate* | kProL2, 0 = plain op).

@@ -202,7 +202,8 @@ __device__ __forceinline__ void prologue(Prep& sm, Inputs<NW>& in, const Prologu
     if constexpr ((PRO & 3) == kGateBounded) {
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
-            const f32x2 g = unpack2(__builtin_bit_cast(uint32_t, in.la[j][0]));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const f32x2 g = unpack2(__builtin_bit_cast(u32x2, in.la[j])[0]);   // raw gate bits in .x
             in.la[j] = f32x2{-pr.bound * sigmoid_f(g[0]), -pr.bound * sigmoid_f(g[1])};
         }
     }
@@ -748,7 +749,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
     using namespace mf;
     constexpr int DVB = NW * 16;
     __shared__ Prep sm;
-    __shared__ bf16 sV[C * (DVB + 8)];
+    __shared__ __attribute__((aligned(16))) bf16 sV[C * (DVB + 8)];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
@@ -914,7 +915,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     using namespace mf;
     constexpr int NW = 8, DVB = 128;
     __shared__ Prep sm;
-    __shared__ bf16 sV[C * (DVB + 8)];
+    __shared__ __attribute__((aligned(16))) bf16 sV[C * (DVB + 8)];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int ngrp = (nch_all + cpw - 1) / cpw;
@@ -1021,7 +1022,7 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
     using namespace mf;
     __shared__ bf16x8 sSB[4][64];        // S as four B operands (32-deep steps)
     __shared__ bf16x4 sUB[2][64][2];     // U as two B operands, halves by token tile
-    __shared__ bf16 sO[4][16 * 16];      // output tiles, token-major
+    __shared__ __attribute__((aligned(16))) bf16 sO[4][16 * 16];   // output tiles, token-major
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;

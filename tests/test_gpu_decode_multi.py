@@ -136,3 +136,16 @@ def test_decode_config_size_draft():
         ro, rS = oracle_multi(xb, [nb])
         report(f"draft config sequence {b} (n={nb})", [("o", o[b:b + 1], ro), ("S", S[b:b + 1], rS)],
                TOL_BF16)
+
+
+@pytest.mark.parametrize("T", [2, 3])
+def test_short_drafts_on_matrix_cores(T):
+    # the bf16 d = 128 draft path for the shortest drafts, accepted counts
+    # from 0 (verify only) to T
+    B, H = 6, 16
+    x = inputs(B, T, H, seed=90 + T)
+    n = [0, 1, T, 1, T - 1, T]
+    o, S = gpu_multi(x, n)
+    ro, rS = oracle_multi(x, n)
+    report(f"multi bf16 B{B} H{H} T{T} n={n}", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+    assert torch.equal(S[0].cpu(), x["S0"][0]), "n_commit = 0 must leave the state untouched"

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <cstring>
 
 #include "kda_launch.h"
 
@@ -305,12 +306,14 @@ struct LayerCfg {
 // each mode has its own element size and per-token count.
 kda_status layer_cfg(const kda_layer_opts* opts, LayerCfg& cfg) {
     if (!opts) return KDA_OK;
-    if (opts->gate != KDA_GATE_LOG && opts->gate != KDA_GATE_BOUNDED &&
-        opts->gate != KDA_GATE_SCALAR)
+    // the mode is read as an int: a C caller may store any value in the field
+    int gate;
+    std::memcpy(&gate, &opts->gate, sizeof gate);
+    if (gate != KDA_GATE_LOG && gate != KDA_GATE_BOUNDED && gate != KDA_GATE_SCALAR)
         return KDA_ERR_INVALID_ARG;
     if (!(opts->decay_bound >= 0.f) || !(opts->l2_eps >= 0.f) || !(opts->out_eps >= 0.f))
         return KDA_ERR_INVALID_ARG;   // negative or NaN
-    cfg.pro = (int)opts->gate | (opts->l2norm_qk ? kda::kProL2 : 0);
+    cfg.pro = gate | (opts->l2norm_qk ? kda::kProL2 : 0);
     if (opts->decay_bound > 0.f) cfg.pr.bound = opts->decay_bound;
     if (opts->l2_eps > 0.f) cfg.pr.l2_eps = opts->l2_eps;
     cfg.z = opts->out_gate;

@@ -295,3 +295,28 @@ def test_deterministic():
     o1, S1 = gpu_prefill(xd)
     o2, S2 = gpu_prefill(xd)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("H", [4, 64])   # prep + state walk; fused
+def test_prefill_then_decode_equals_prefill_of_concatenation(H):
+    # serving's hand-over: prefill a prompt, then decode token by token from
+    # its final state; the same tokens prefilled in one call must agree
+    c = W.PREFILL_CONFIGS["batched"]
+    B, T, m = 4, 150, 6
+    x = W.prefill_inputs(c, B=B, T=T + m, H=H)
+    xd = to_dev(x)
+    head = {n: (v[:, :T].contiguous() if n != "S0" else v) for n, v in xd.items()}
+    _, S = gpu_prefill(head)
+    outs = []
+    for t in range(T, T + m):
+        step = {n: xd[n][:, t].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")}
+        outs.append(kda.kda_decode_step(step["q"], step["k"], step["v"], step["log_alpha"],
+                                        step["beta"], S))
+    torch.cuda.synchronize()
+    o_all, S_all = gpu_prefill(xd)
+    o_dec = torch.stack(outs, dim=1)
+    report(f"prefill T{T} + {m} decode steps vs prefill T{T + m}, H{H}",
+           [("o", o_dec, o_all[:, T:].cpu().double().numpy()),
+            ("S", S, S_all.cpu().double().numpy())], TOL_BF16)
+    ro, rS = oracle_prefill(x)
+    report(f"prefill + decode vs oracle, H{H}", [("o", o_dec, ro[:, T:]), ("S", S, rS)], TOL_BF16)

@@ -201,7 +201,7 @@ def bench_decode_multi(cfg, T=8, reps=20):
                      "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9,
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                  "kernel": "decode_multi_kernel", "algorithmic_bytes": nbytes}}
+                                  "kernel": "decode_multi_mfma_kernel", "algorithmic_bytes": nbytes}}
     out["workload"] = f"kda_decode_multi B{cfg.B} H{cfg.H} dk{cfg.dk} dv{cfg.dv} T{T} bf16"
     return out
 

@@ -189,15 +189,16 @@ def test_split_sequence_continuation():
     report("split vs one shot", [("S", Sb, S.cpu().double().numpy())], 5e-3)
 
 
-def test_state_in_place():
+@pytest.mark.parametrize("B,H", [(1, 2), (2, 64), (4, 64)])   # split, fused 64- and 128-column
+def test_state_in_place(B, H):
     c = W.PREFILL_CONFIGS["batched"]
-    x = W.prefill_inputs(c, B=1, T=130, H=2)
+    x = W.prefill_inputs(c, B=B, T=130, H=H)
     xd = to_dev(x)
     S = xd["S0"].clone()
     o, Sf = gpu_prefill(xd, S0=S, S_final=S)
     assert Sf.data_ptr() == S.data_ptr()
     ro, rS = oracle_prefill(x)
-    report("in-place S_final = S0", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+    report(f"in-place S_final = S0, B{B} H{H}", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
 def test_empty_sequence_copies_state():

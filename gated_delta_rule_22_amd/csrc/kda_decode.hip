@@ -77,12 +77,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const int col = slice * NC + cg * 4;
     const int row0 = rg * RPL;
 
+    // (plain loads measured about 2% faster here than streaming ones; the
+    // stores below stream)
     float* Sh = S + (size_t)hd * DK * DV;
     f32x4 s[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-        s[r] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(Sh + (size_t)(row0 + r) * DV + col));
+        s[r] = *reinterpret_cast<const f32x4*>(Sh + (size_t)(row0 + r) * DV + col);
 
     float kr[RPL], qr[RPL], lar[RPL];
     load_row_vals<T, RPL>(k + (size_t)hd * DK + row0, kr);

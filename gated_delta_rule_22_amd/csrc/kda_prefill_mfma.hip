@@ -152,7 +152,7 @@ struct Inputs {
 // Loads are unconditional (tail tokens re-read the last token) and the raw
 // values are kept as loaded: tail tokens are zeroed where they are consumed,
 // so no instruction waits on a load before the next chunk is needed.
-template <int NW, int DVB, int PRO>
+template <int NW, int DVB, int PRO, bool NT = false>
 __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k,
                                             const bf16* __restrict__ v,
@@ -171,10 +171,16 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
     for (int j = 0; j < TPT; ++j) {
         const size_t rw = row(c * C + t0 + j);
         const size_t base = rw * DK + 2 * lane;
-        in.k[j] = *reinterpret_cast<const uint32_t*>(k + base);
-        in.q[j] = *reinterpret_cast<const uint32_t*>(q + base);
+        if constexpr (NT) {
+            in.k[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(k + base));
+            in.q[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + base));
+        } else {
+            in.k[j] = *reinterpret_cast<const uint32_t*>(k + base);
+            in.q[j] = *reinterpret_cast<const uint32_t*>(q + base);
+        }
         if constexpr (GM == kGateLog) {
-            in.la[j] = *reinterpret_cast<const f32x2*>(static_cast<const float*>(gate) + base);
+            const f32x2* lp = reinterpret_cast<const f32x2*>(static_cast<const float*>(gate) + base);
+            in.la[j] = NT ? __builtin_nontemporal_load(lp) : *lp;
         } else if constexpr (GM == kGateBounded) {
             const uint32_t bits = *reinterpret_cast<const uint32_t*>(static_cast<const bf16*>(gate) + base);
             in.la[j] = f32x2{__builtin_bit_cast(float, bits), 0.f};
@@ -928,7 +934,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     ChunkPos p{0, 1, 0};
     if (gc0 < gc1) {
         p = map.at(gc0);
-        load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, p.tok0, p.len, h, H, p.c, 0);
+        load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, p.tok0, p.len, h, H, p.c, 0);
     }
     for (int gc = gc0; gc < gc1; ++gc) {
         const int ntok = p.len - p.c * C;
@@ -943,10 +949,10 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         else stage1b<NW, false, PRO>(sm, in, ntok, fast);
         // next chunk's inputs: waves 0-3 now; waves 4-7 (lighter Gram work)
         // after stage 2, so their fetches queue while the inverses finish
-        if (more && wave < 4) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        if (more && wave < 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         stage2<NW>(sm, fast);
-        if (more && wave >= 4) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
@@ -1237,7 +1243,8 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
                 if (decltype(full)::value || 16 * I < nt) {
                     const int t = decltype(full)::value ? 16 * I + tt : min(16 * I + tt, nt - 1);
                     const uint2 v = *reinterpret_cast<const uint2*>(&tile[(t - 16 * I) * 16 + tc]);
-                    *reinterpret_cast<uint2*>(o + (((size_t)tok0 + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc) = v;
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(o + (((size_t)tok0 + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc));
                 }
             });
         };

@@ -37,6 +37,56 @@ constexpr int RS = 16 + 8;        // bf16 row stride of K_restore^T [D][16 token
 constexpr int kBufWord3 = 0x00020000;
 constexpr int kNT = 2;
 
+// 4x4 transpose across the four lanes of a quad: lane p holds x = M[p][0..3]
+// and receives M[0..3][p]. Two butterfly steps, each taking the partner
+// lane's element through a DPP quad permute (partners p ^ 1, then p ^ 2) for
+// the positions whose index bit differs from the lane's.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x) {
+    const int p = threadIdx.x & 3;
+    float a[4], b[4], v[4] = {x[0], x[1], x[2], x[3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float t = dpp_f<0xB1>(v[e ^ 1]);   // quad_perm [1,0,3,2]
+        a[e] = ((e ^ p) & 1) ? t : v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float t = dpp_f<0x4E>(a[e ^ 2]);   // quad_perm [2,3,0,1]
+        b[e] = ((e ^ p) & 2) ? t : a[e];
+    }
+    return f32x4{b[0], b[1], b[2], b[3]};
+}
+
+// Swap of 16-lane rows between two registers (v_permlane16_swap): a keeps
+// its rows 0 and 2 and takes b's rows 0 and 2 as its rows 1 and 3; b keeps
+// its rows 1 and 3 and takes a's rows 1 and 3 as its rows 0 and 2. It is its
+// own inverse.
+__device__ __forceinline__ void row_swap(f32x4& a, f32x4& b) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 ua = __builtin_bit_cast(u32x4, a), ub = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(ua[e], ub[e], false, false);
+        ua[e] = sw[0];
+        ub[e] = sw[1];
+    }
+    a = __builtin_bit_cast(f32x4, ua);
+    b = __builtin_bit_cast(f32x4, ub);
+}
+
+// Two 8-row loads (lane rows: 16-column tile 0 and 1 of rows +0..3, then the
+// same of rows +4..7) -> the two accumulator tiles of those 16 rows; and back.
+__device__ __forceinline__ void tiles_from_rows(f32x4& a, f32x4& b) {
+    a = quad_transpose(a);
+    b = quad_transpose(b);
+    row_swap(a, b);
+}
+__device__ __forceinline__ void rows_from_tiles(f32x4& a, f32x4& b) {
+    row_swap(a, b);
+    a = quad_transpose(a);
+    b = quad_transpose(b);
+}
+
 __device__ __forceinline__ bf16x8 ldA_perm8(const bf16* rowp, int k0, int g) {
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(rowp + k0 + 4 * g);
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(rowp + k0 + 16 + 4 * g);
@@ -71,18 +121,22 @@ __global__ __launch_bounds__(256) void decode_multi_mfma_kernel(
     int n = n_commit ? n_commit[bb] : T;
     n = __builtin_amdgcn_readfirstlane(min(max(n, 0), T));
 
-    // ---- state slice, accumulator layout: Sa[m][ct] = rows 16m + 4g + i, column c0 + 16ct + r
-    // (buffer loads: a per-head resource, eight per-lane byte offsets and a
-    // uniform offset per 16-row block, so no per-element 64-bit address
-    // stays live until the store; nt = streaming, as in the decode step)
+    // ---- state slice: this wave's 32 columns c0 .. c0 + 31 of all 128 rows.
+    // It moves in whole 128-byte row pieces: load j brings rows 8j .. 8j + 7,
+    // lane (hh = l / 32, cq = (l / 4) % 8, p = l % 4) holding row 8j + 4hh + p,
+    // columns c0 + 4cq .. + 3. A transpose within each quad of lanes then
+    // gives every lane four rows of one column, and a row swap between the
+    // loads 2m and 2m + 1 (v_permlane16_swap) gathers each 16-column tile, so
+    // that st[m][ct] is an MFMA accumulator tile: lane (g, r) holds column
+    // c0 + 16ct + r of rows 16m + 4 sig(g) + i, sig(g) = (0, 2, 1, 3)[g]
+    // (the A operands below index their rows with the same permutation). The
+    // store runs the steps backwards. Buffer accesses: a per-head resource,
+    // one per-lane byte offset and a uniform offset per 8-row load.
     float* Sh = S + (size_t)head * D * D;
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(Sh, 0, D * D * 4, kBufWord3);
     const int c0 = 32 * wave;
-    int off[2][4];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) off[ct][i] = ((4 * g + i) * D + c0 + 16 * ct + r) * 4;
+    const int off = ((4 * (lane >> 5) + (lane & 3)) * D + c0 + 4 * ((lane >> 2) & 7)) * 4;
+    const int sig = ((g & 1) << 1) | (g >> 1);   // row quarter held by lane group g
     // ---- token side: one thread per channel d; threads 0-127 the key side
     //      (k, and the value column d), 128-255 the query side. All token
     //      loads are issued first.
@@ -107,14 +161,13 @@ __global__ __launch_bounds__(256) void decode_multi_mfma_kernel(
     // overlaps the token-side work; the W pass and the commit then use it
     // from registers. Streaming (nt) accesses: each element is read once and
     // written at most once.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     f32x4 st[8][2];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st[m][ct][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, off[ct][i], 16 * m * D * 4, kNT));
+        for (int h = 0; h < 2; ++h)   // loads 2m + h, gathered into tiles below
+            st[m][h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, (2 * m + h) * 8 * D * 4, kNT));
     float x_t[TM], vcol[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
@@ -182,10 +235,13 @@ __global__ __launch_bounds__(256) void decode_multi_mfma_kernel(
     // ---- W = [K_decay; Q_decay] S on the matrix cores, 32 state rows per
     //      step: the B operand of step kk is this lane's part of the tiles
     //      2kk and 2kk + 1 (rows 32kk + 4g + i and 32kk + 16 + 4g + i)
+    // (row pieces to accumulator tiles, once the loads are in)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) tiles_from_rows(st[m][0], st[m][1]);
     f32x4 Wc[2] = {zero4(), zero4()};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = ldA_perm8(sA + r * AS, 32 * kk, g);
+        const bf16x8 a = ldA_perm8(sA + r * AS, 32 * kk, sig);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) Wc[ct] = mma32(a, pack8(st[2 * kk][ct], st[2 * kk + 1][ct]), Wc[ct]);
     }
@@ -226,9 +282,6 @@ __global__ __launch_bounds__(256) void decode_multi_mfma_kernel(
     //      decayed, updated on the matrix cores in fp32 and written back
     if (n == 0) return;   // verify pass: the state is only read (uniform)
     __syncthreads();
-    // (the whole vector is bit-cast, then indexed: a bit cast of one vector
-    // element has been seen to lose the element index here)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     s16x4 b[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
@@ -236,15 +289,18 @@ __global__ __launch_bounds__(256) void decode_multi_mfma_kernel(
         for (int i = 0; i < 4; ++i) b[ct][i] = __builtin_bit_cast(short, sU[(4 * g + i) * AS + c0 + 16 * ct + r]);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const f32x4 dal = *reinterpret_cast<const f32x4*>(&sDal[16 * m + 4 * g]);
-        const s16x4 a = *reinterpret_cast<const s16x4*>(&sKrT[(16 * m + r) * RS + 4 * g]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const u32x4 bits = __builtin_bit_cast(u32x4, mma16(a, b[ct], st[m][ct] * dal));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(bits[i], srs, off[ct][i], 16 * m * D * 4, kNT);
-        }
+        // (accumulator row 4g + i is state row 16m + 4 sig(g) + i; the A
+        // operand's row r likewise stands for state row 16m + 4 sig(r / 4) + r % 4)
+        const f32x4 dal = *reinterpret_cast<const f32x4*>(&sDal[16 * m + 4 * sig]);
+        const int ar = 4 * (((r >> 2) & 1) << 1 | (r >> 3)) + (r & 3);
+        const s16x4 a = *reinterpret_cast<const s16x4*>(&sKrT[(16 * m + ar) * RS + 4 * g]);
+        f32x4 t0 = mma16(a, b[0], st[m][0] * dal);
+        f32x4 t1 = mma16(a, b[1], st[m][1] * dal);
+        rows_from_tiles(t0, t1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t0), srs, off,
+                                               (2 * m) * 8 * D * 4, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t1), srs, off,
+                                               (2 * m + 1) * 8 * D * 4, kNT);
     }
 }
 

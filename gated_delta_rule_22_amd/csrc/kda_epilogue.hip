@@ -36,9 +36,13 @@ __global__ __launch_bounds__(kEpiWaves * 64) void norm_gate_kernel(
 #pragma unroll
     for (int e = 0; e < VEC; ++e) wv[e] = w ? w[c0 + e] : 1.f;
 
-    const long wave = (long)blockIdx.x * kEpiWaves + (threadIdx.x >> 6);
-    const long nwaves = (long)gridDim.x * kEpiWaves;
-    for (long r0 = wave * (RPW * kUnroll); r0 < rows; r0 += nwaves * (RPW * kUnroll)) {
+    // The workgroup walks the rows in blocks of kEpiWaves * RPW * kUnroll, all
+    // its waves taking the same number of steps, and the waves meet once
+    // their loads are in so that they stream neighbouring rows together.
+    constexpr long kBlockRows = (long)kEpiWaves * RPW * kUnroll;
+    const long wave_rows = (long)(threadIdx.x >> 6) * (RPW * kUnroll);
+    for (long b0 = (long)blockIdx.x * kBlockRows; b0 < rows; b0 += (long)gridDim.x * kBlockRows) {
+        const long r0 = b0 + wave_rows;
         vecT x[kUnroll], g[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -46,6 +50,7 @@ __global__ __launch_bounds__(kEpiWaves * 64) void norm_gate_kernel(
             x[u] = *reinterpret_cast<const vecT*>(o + row * DV + c0);
             g[u] = *reinterpret_cast<const vecT*>(z + row * DV + c0);
         }
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float xf[VEC], sq = 0.f;

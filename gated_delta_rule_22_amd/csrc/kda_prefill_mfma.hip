@@ -277,8 +277,9 @@ __device__ __forceinline__ bool chunk_is_mild(const Prep& sm) {
 // Stage 1b: decay-scaled operands. Thread (range = wave, channels 2*lane, +1).
 // The decay reference is the chunk start when `fast`, else the start of the
 // token's 16-token block. FULL: every token of the chunk is real.
-template <int NW, bool FULL, int PRO>
-__device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok, bool fast) {
+template <int NW, bool FULL, int PRO, bool FAST>
+__device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok) {
+    constexpr bool fast = FAST;
     constexpr int TPT = C / NW;
     constexpr int SPB = NW / 4;      // token ranges per 16-token block
     const int lane = threadIdx.x & 63, wave = wave_id();
@@ -309,15 +310,16 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
     const f32x2 eR = {exp_e(tail[0]), exp_e(tail[1])};
     const f32x2 eP = fast ? f32x2{1.f, 1.f} : f32x2{exp_e(head[0]), exp_e(head[1])};
 
-    // chunk-level factors, spread over the first four token ranges
-    if (wave == 0) {
+    // chunk-level factors, spread over the first four token ranges (the
+    // block decays P and G serve the block reference only)
+    if (!fast && wave == 0) {
         f32x2 acc = {0.f, 0.f};
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             *reinterpret_cast<float2*>(&sm.P[I * DK + d0]) = make_float2(exp_e(acc[0]), exp_e(acc[1]));
             acc += tau[I];
         }
-    } else if (wave == 1 || wave == 2) {
+    } else if (!fast && (wave == 1 || wave == 2)) {
         // G for pairs (1,0),(2,0),(2,1) on range 1 and (3,0),(3,1),(3,2) on range 2
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
@@ -358,8 +360,13 @@ __device__ __forceinline__ void stage1b(Prep& sm, const Inputs<NW>& in, int ntok
         kr0[j] = ki[0] * eR[0];                              // decay t+1 .. chunk end
         kr1[j] = ki[1] * eR[1];
         const float bta = sm.beta[t];
-        rk0[j] = bta * kd[0] * eP[0];                        // beta_t k_t decay(start .. t)
-        rk1[j] = bta * kd[1] * eP[1];
+        if constexpr (fast) {                                // beta_t k_t decay(start .. t)
+            rk0[j] = bta * kd[0];
+            rk1[j] = bta * kd[1];
+        } else {
+            rk0[j] = bta * kd[0] * eP[0];
+            rk1[j] = bta * kd[1] * eP[1];
+        }
     }
     auto put8 = [&](bf16* dst, const float* x) {
         *reinterpret_cast<uint4*>(dst) = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]),
@@ -793,8 +800,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
         const bool fast = chunk_is_mild<NW>(sm);
-        if (ntok >= C) stage1b<NW, true, PRO>(sm, in, ntok, fast);
-        else stage1b<NW, false, PRO>(sm, in, ntok, fast);
+        if (fast) {
+            if (ntok >= C) stage1b<NW, true, PRO, true>(sm, in, ntok);
+            else stage1b<NW, false, PRO, true>(sm, in, ntok);
+        } else {
+            if (ntok >= C) stage1b<NW, true, PRO, false>(sm, in, ntok);
+            else stage1b<NW, false, PRO, false>(sm, in, ntok);
+        }
         // next chunk's inputs; with 8 waves, waves 4-7 (lighter Gram work)
         // fetch after stage 2, so their fetches queue while the inverses finish
         const bool early_fetch = NW < 8 || wave < 4;
@@ -945,8 +957,13 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         stage1a<NW, DVB>(sm, sV, in, ntok);
         lds_barrier();
         const bool fast = chunk_is_mild<NW>(sm);
-        if (ntok >= C) stage1b<NW, true, PRO>(sm, in, ntok, fast);
-        else stage1b<NW, false, PRO>(sm, in, ntok, fast);
+        if (fast) {
+            if (ntok >= C) stage1b<NW, true, PRO, true>(sm, in, ntok);
+            else stage1b<NW, false, PRO, true>(sm, in, ntok);
+        } else {
+            if (ntok >= C) stage1b<NW, true, PRO, false>(sm, in, ntok);
+            else stage1b<NW, false, PRO, false>(sm, in, ntok);
+        }
         // next chunk's inputs: waves 0-3 now; waves 4-7 (lighter Gram work)
         // after stage 2, so their fetches queue while the inverses finish
         if (more && wave < 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);

@@ -483,8 +483,11 @@ __device__ __forceinline__ void stage2(Prep& sm, bool fast) {
 // Block I: Y_I -= sum_{J<I} L_IJ X_J, then X_I = D_I Y_I (accumulator order,
 // feeds later blocks as the B operand) and, for W, X_I^T = Y_I^T D_I^T: its
 // accumulator holds W rows in A-operand order, stored straight into NWop.
-template <int NW, int DVB>
-__device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x4 (&U0)[4], bool fast) {
+struct NoHook { __device__ void operator()(int) const {} };
+
+template <int NW, int DVB, typename Hook = NoHook>
+__device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x4 (&U0)[4], bool fast,
+                                       Hook hook = Hook()) {
     constexpr int VS = DVB + 8;
     constexpr int NWT = 8 / NW;
     constexpr int NTILE = NWT + 1;
@@ -498,6 +501,9 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
         const float2 f = *reinterpret_cast<const float2*>(&sm.P[(t >> 4) * DK + d]);
         *p = pack2(a[0] * f.x, a[1] * f.y);
     }
+    // a hook that reads Q_decay needs the scaling above from every thread
+    if constexpr (!std::is_same<Hook, NoHook>::value)
+        if (!fast) lds_barrier();
 
     f32x4 X[NTILE][4];
 #pragma unroll
@@ -534,6 +540,7 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
                     __builtin_convertvector(-xt, bf16x4);
             }
         }
+        hook(I);
     }
 #pragma unroll
     for (int I = 0; I < 4; ++I) U0[I] = X[NWT][I];
@@ -971,18 +978,15 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         stage2<NW>(sm, fast);
         if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
-        f32x4 U0[4];
-        stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
-        lds_barrier();
-        p = pn;
         char* rec = ws + ((size_t)h * nch_all + gc) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
-        // 54 A operands, spread over the waves: 16 B per lane each. Seven per
-        // wave; waves 6, 7 store their sixth operand twice (same data, same
-        // address) so that every wave issues a fixed number of stores.
-#pragma unroll
-        for (int jj = 0; jj < 7; ++jj) {
-            const int j = (wave + NW * jj < 54) ? wave + NW * jj : wave + NW * (jj - 1);
+        // 54 A operands, 16 B per lane each. The 38 that are final before
+        // the substitution (Q_decay, M_qk, K_restore^T) leave during it,
+        // five per wave, one or two after each block, so that their stores
+        // overlap its matrix work; waves 6, 7 store their fifth twice (same
+        // data, same address). The 16 -W operands follow it, two per wave.
+        // Every wave thus issues a fixed number of stores.
+        auto store_op = [&](int j) {
             bf16x8 val;
             int off;
             if (j < 16) {              // -W (I = j / 4, kk = j % 4)
@@ -997,7 +1001,19 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
                 val = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g); off = REC_KR + jj * OPB;
             }
             *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = val;
-        }
+        };
+        auto early = [&](int I) {
+#pragma unroll
+            for (int jj = 0; jj < 5; ++jj)
+                if (jj == I || (I == 3 && jj == 4))
+                    store_op(16 + ((wave + NW * jj < 38) ? wave + NW * jj : wave + NW * (jj - 1)));
+        };
+        f32x4 U0[4];
+        stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast, early);
+        lds_barrier();
+        p = pn;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) store_op(wave + NW * jj);
         if (wave == 0)   // lanes 32-63 repeat lanes 0-31
             *reinterpret_cast<f32x4*>(rec + REC_AL + (lane & 31) * 16) =
                 *reinterpret_cast<const f32x4*>(&sm.alast[4 * (lane & 31)]);

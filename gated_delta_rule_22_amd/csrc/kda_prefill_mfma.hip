@@ -485,9 +485,11 @@ __device__ __forceinline__ void stage2(Prep& sm, bool fast) {
 // accumulator holds W rows in A-operand order, stored straight into NWop.
 struct NoHook { __device__ void operator()(int) const {} };
 
-template <int NW, int DVB, typename Hook = NoHook>
+// NWG: -W goes straight from registers to the operand record at nw_rec
+// (each wave its own 8-byte half of each operand) instead of to sm.NWop.
+template <int NW, int DVB, typename Hook = NoHook, bool NWG = false>
 __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x4 (&U0)[4], bool fast,
-                                       Hook hook = Hook()) {
+                                       Hook hook = Hook(), char* nw_rec = nullptr) {
     constexpr int VS = DVB + 8;
     constexpr int NWT = 8 / NW;
     constexpr int NTILE = NWT + 1;
@@ -536,8 +538,11 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
             if (tl < NWT) {
                 const f32x4 xt = mma16(yb, dI, zero4());
                 const int dt = wave + tl * NW;                // channel tile
-                reinterpret_cast<bf16x4*>(&sm.NWop[I * 4 + (dt >> 1)][lane])[dt & 1] =
-                    __builtin_convertvector(-xt, bf16x4);
+                const bf16x4 nw = __builtin_convertvector(-xt, bf16x4);
+                if constexpr (NWG)
+                    *reinterpret_cast<bf16x4*>(nw_rec + REC_NW + (I * 4 + (dt >> 1)) * OPB + lane * 16 + (dt & 1) * 8) = nw;
+                else
+                    reinterpret_cast<bf16x4*>(&sm.NWop[I * 4 + (dt >> 1)][lane])[dt & 1] = nw;
             }
         }
         hook(I);
@@ -980,18 +985,18 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         lds_barrier();
         char* rec = ws + ((size_t)h * nch_all + gc) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
-        // 54 A operands, 16 B per lane each. The 38 that are final before
-        // the substitution (Q_decay, M_qk, K_restore^T) leave during it,
-        // five per wave, one or two after each block, so that their stores
-        // overlap its matrix work; waves 6, 7 store their fifth twice (same
-        // data, same address). The 16 -W operands follow it, two per wave.
-        // Every wave thus issues a fixed number of stores.
-        auto store_op = [&](int j) {
+        // 54 A operands, 16 B per lane each, all stored during the
+        // substitution so that the stores overlap its matrix work: the 38
+        // that are final before it (Q_decay, M_qk, K_restore^T) five per
+        // wave, one or two after each block (waves 6, 7 store their fifth
+        // twice: same data, same address), and -W straight from the
+        // registers that form it, each wave its 8-byte half of the four
+        // operands of its channel tile. Every wave thus issues a fixed
+        // number of stores.
+        auto store_op = [&](int j) {  // j in 16 .. 53: the operands after -W
             bf16x8 val;
             int off;
-            if (j < 16) {              // -W (I = j / 4, kk = j % 4)
-                val = sm.NWop[j][lane]; off = REC_NW + j * OPB;
-            } else if (j < 32) {       // Q_decay
+            if (j < 32) {              // Q_decay
                 const int jj = j - 16;
                 val = ldA_perm(sm.Qd + (16 * (jj >> 2) + r) * KS, 32 * (jj & 3), g); off = REC_QD + jj * OPB;
             } else if (j < 38) {       // M_qk
@@ -1009,11 +1014,8 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
                     store_op(16 + ((wave + NW * jj < 38) ? wave + NW * jj : wave + NW * (jj - 1)));
         };
         f32x4 U0[4];
-        stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast, early);
-        lds_barrier();
+        stage3<NW, DVB, decltype(early), true>(sm, sV, 16 * wave, U0, fast, early, rec);
         p = pn;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) store_op(wave + NW * jj);
         if (wave == 0)   // lanes 32-63 repeat lanes 0-31
             *reinterpret_cast<f32x4*>(rec + REC_AL + (lane & 31) * 16) =
                 *reinterpret_cast<const f32x4*>(&sm.alast[4 * (lane & 31)]);

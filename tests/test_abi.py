@@ -227,3 +227,15 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 1, 16)
     with pytest.raises(ValueError):
         kda.kda_prefill_fwd(x, x, x, x, torch.zeros(1, 4, 1))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback: without the built HIP library every entry point raises
+    import gated_delta_rule_22_amd as kda_mod
+    monkeypatch.setattr(kda_mod, "_lib", None)
+    monkeypatch.setattr(kda_mod, "_LIB_PATH", str(tmp_path / "libkda.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        kda_mod.load_library()
+    import torch
+    with pytest.raises(RuntimeError, match="missing"):
+        kda_mod.kda_prefill_workspace_size(1, 64, 2, 128, 128, torch.bfloat16)

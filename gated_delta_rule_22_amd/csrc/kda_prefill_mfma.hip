@@ -980,11 +980,24 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         // after stage 2, so their fetches queue while the inverses finish
         if (more && wave < 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
-        stage2<NW>(sm, fast);
-        if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
-        lds_barrier();
         char* rec = ws + ((size_t)h * nch_all + gc) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
+        stage2<NW>(sm, fast);
+        // Q_decay operands 4(w - 4) .. + 3 (block I = w - 4): on the chunk
+        // reference they are final since stage 1, and waves 4-7 store them
+        // here, in their slack while the inverses finish; otherwise (scaled
+        // in stage 3) after the substitution's block 0
+        auto store_qd = [&]() {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int j = 4 * (wave - 4) + kk;
+                *reinterpret_cast<bf16x8*>(rec + REC_QD + j * OPB + lane * 16) =
+                    ldA_perm(sm.Qd + (16 * (j >> 2) + r) * KS, 32 * kk, g);
+            }
+        };
+        if (fast && wave >= 4) store_qd();
+        if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        lds_barrier();
         // 54 A operands, 16 B per lane each, all stored during the
         // substitution so that the stores overlap its matrix work: the 38
         // that are final before it (Q_decay, M_qk, K_restore^T) five per
@@ -993,25 +1006,20 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         // registers that form it, each wave its 8-byte half of the four
         // operands of its channel tile. Every wave thus issues a fixed
         // number of stores.
-        auto store_op = [&](int j) {  // j in 16 .. 53: the operands after -W
+        auto store_op = [&](int j) {  // j in 0 .. 21: M_qk, then K_restore^T (m = jj / 2, kk = jj % 2)
             bf16x8 val;
             int off;
-            if (j < 32) {              // Q_decay
-                const int jj = j - 16;
-                val = ldA_perm(sm.Qd + (16 * (jj >> 2) + r) * KS, 32 * (jj & 3), g); off = REC_QD + jj * OPB;
-            } else if (j < 38) {       // M_qk
-                val = sm.Mop[j - 32][lane]; off = REC_M + (j - 32) * OPB;
-            } else {                   // K_restore^T (m = jj / 2, kk = jj % 2)
-                const int jj = j - 38;
+            if (j < 6) {
+                val = sm.Mop[j][lane]; off = REC_M + j * OPB;
+            } else {
+                const int jj = j - 6;
                 val = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g); off = REC_KR + jj * OPB;
             }
             *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = val;
         };
         auto early = [&](int I) {
-#pragma unroll
-            for (int jj = 0; jj < 5; ++jj)
-                if (jj == I || (I == 3 && jj == 4))
-                    store_op(16 + ((wave + NW * jj < 38) ? wave + NW * jj : wave + NW * (jj - 1)));
+            if (I < 3) store_op((wave + NW * I < 22) ? wave + NW * I : wave + NW * (I - 1));
+            if (I == 0 && !fast && wave >= 4) store_qd();
         };
         f32x4 U0[4];
         stage3<NW, DVB, decltype(early), true>(sm, sV, 16 * wave, U0, fast, early, rec);

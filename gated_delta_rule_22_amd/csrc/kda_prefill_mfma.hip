@@ -996,6 +996,16 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
             }
         };
         if (fast && wave >= 4) store_qd();
+        // K_restore^T (final since stage 1 on either reference): waves 6, 7,
+        // the two with a single Gram pair, store its 16 operands here
+        if (wave >= 6) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = 8 * (wave - 6) + e;   // m = jj / 2, kk = jj % 2
+                *reinterpret_cast<bf16x8*>(rec + REC_KR + jj * OPB + lane * 16) =
+                    ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g);
+            }
+        }
         if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         // 54 A operands, 16 B per lane each, all stored during the
@@ -1006,19 +1016,10 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         // registers that form it, each wave its 8-byte half of the four
         // operands of its channel tile. Every wave thus issues a fixed
         // number of stores.
-        auto store_op = [&](int j) {  // j in 0 .. 21: M_qk, then K_restore^T (m = jj / 2, kk = jj % 2)
-            bf16x8 val;
-            int off;
-            if (j < 6) {
-                val = sm.Mop[j][lane]; off = REC_M + j * OPB;
-            } else {
-                const int jj = j - 6;
-                val = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g); off = REC_KR + jj * OPB;
-            }
-            *reinterpret_cast<bf16x8*>(rec + off + lane * 16) = val;
-        };
         auto early = [&](int I) {
-            if (I < 3) store_op((wave + NW * I < 22) ? wave + NW * I : wave + NW * (I - 1));
+            // M_qk: one operand each for waves 0-5 after block 0
+            if (I == 0 && wave < 6)
+                *reinterpret_cast<bf16x8*>(rec + REC_M + wave * OPB + lane * 16) = sm.Mop[wave][lane];
             if (I == 0 && !fast && wave >= 4) store_qd();
         };
         f32x4 U0[4];

@@ -2,22 +2,25 @@
 """KDA prefill / decode throughput on one MI355X.
 
 One JSON line on stdout. The headline (``value``) is prefill tokens/s on the
-workload chosen with --workload (default: B=1, H=16, T=4096, d=128, chunk 64,
-bf16 q/k/v, fp32 state). A "step" is one full prefill of that batch: one call
-of kda_prefill_fwd, i.e. chunk cumsum and decay scaling, intra-chunk Gram,
-UT inverse, pseudo-values, outputs and the state carry (for few heads a
-chunk-parallel prep launch followed by the state-walk launch; the roofline
-covers both, timed together with HIP events on their stream). Inputs are resident
-in HBM before timing; each timed step reads its own replica of the batch so
-the 256 MB last-level cache cannot hold the inputs between steps.
+workload chosen with --workload (default: the 1M-token context, B=1, H=32,
+T=1,048,576, d=128, chunk 64, bf16 q/k/v, fp32 state: the largest
+single-GPU configuration). A "step" is one full prefill of that batch: one
+call of kda_prefill_fwd, i.e. chunk cumsum and decay scaling, intra-chunk
+Gram, UT inverse, pseudo-values, outputs and the state carry (for few heads
+a chunk-parallel prep launch followed by the state-walk launch; the roofline
+covers both, timed together with HIP events on their stream). Inputs are
+resident in HBM before timing; when a batch is small enough to stay in the
+256 MB last-level cache, each timed step reads its own replica of it.
 
-Also reported in the same line: the decode workload (B=256, H=32, d=128, 1024
-sequential steps, fp32 state of 537 MB streamed per step) as "decode", an
-8-token draft verified and committed from that state as "decode_multi", a
-packed batch of 18 prompts of mixed length (65,536 tokens, H=32) with state
-checkpoints every 512 tokens as "varlen", the roofline of the dominant kernel
-timed with HIP events on its stream, and the fp64 CPU oracle timed on the host
-cores over a bounded sample.
+Also reported in the same line: the other two bf16 prefill configurations
+(B=1 H=16 T=4096 as "prefill_4k", B=8 H=32 T=8192 with a carried state as
+"batched"), each with its own roofline; the decode workload (B=256, H=32,
+d=128, 1024 sequential steps, fp32 state of 537 MB streamed per step) as
+"decode", an 8-token draft verified and committed from that state as
+"decode_multi", a packed batch of 18 prompts of mixed length (65,536 tokens,
+H=32) with state checkpoints every 512 tokens as "varlen", the layer form as
+"layer", and the fp64 CPU oracle timed on the host cores over a bounded
+sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -79,7 +82,10 @@ def bench_prefill(cfg, steps, warmup):
     from workloads import accounting as A
 
     dev = torch.device("cuda:0")
-    x = W.prefill_inputs(cfg, device=dev)
+    # a single long sequence is drawn head by head (per-head seeds), as the
+    # parity tests draw it
+    x = (W.prefill_inputs_by_head(cfg, device=dev) if cfg.name == "long"
+         else W.prefill_inputs(cfg, device=dev))
     per_batch = sum(t.numel() * t.element_size() for t in x.values() if t is not None)
     reps = max(1, min(steps + warmup, math.ceil(2 * LLC_BYTES / per_batch)))
     batches = [x] + [{n: (t.clone() if t is not None else None) for n, t in x.items()}
@@ -118,6 +124,8 @@ def bench_prefill(cfg, steps, warmup):
     nbytes = A.prefill_bytes(cfg.B, cfg.T, cfg.H, cfg.dk, cfg.dv, elt=2,
                              has_s0=cfg.s0_std > 0, writes_state=True)
     t = kern_ms * 1e-3
+    del batches, outs, ws, x
+    torch.cuda.empty_cache()
     return dict(wall_s=wall, ms_per_step=wall * 1e3 / steps, kernel_ms=kern_ms,
                 tokens_per_s=tokens * steps / wall, flops=flops, flops_cons=flops_c,
                 bytes=nbytes, gbs=nbytes / t / 1e9, tflops=flops / t / 1e12,
@@ -342,10 +350,36 @@ def bench_layer(cfg, reps=20):
     return out
 
 
-def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18, min_seconds=10.0):
+def prefill_roofline(pre, workload):
+    kernels = ("prefill_prep_kernel + prefill_state_kernel" if pre["workspace_bytes"] > 0
+               else "prefill_fused_kernel")
+    return {"bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": pre["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic("prefill", workload),
+            "kernel": kernels, "kernel_us": pre["kernel_ms"] * 1e3,
+            "algorithmic_bytes": pre["bytes"]}
+
+
+def prefill_mfma(pre):
+    return {"flops_per_step": pre["flops"], "achieved_tflops": pre["tflops"],
+            "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pre["tflops"] / MFMA_BF16_PEAK_TFLOPS,
+            "frac_without_inverse": pre["tflops_cons"] / MFMA_BF16_PEAK_TFLOPS}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 16, min_seconds=10.0):
     """fp64 oracle on the host cores over a bounded sample of the same
     workload: whole heads (one per thread) over the first tokens of the
-    sequence. Inputs are converted before the clock starts."""
+    sequence (the same per-head draws). Inputs are converted before the clock
+    starts."""
     import oracle
     import workloads as W
 
@@ -368,19 +402,22 @@ def cpu_baseline_prefill(cfg, max_heads, max_tokens=1 << 18, min_seconds=10.0):
         if dt >= min_seconds:
             break
     # token-heads per second over the sample, as tokens/s of the full workload
-    tps = passes * heads * T / dt / cfg.H
+    tps = passes * heads * T / dt / (cfg.B * cfg.H)
     return dict(value=tps, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{heads} of {cfg.H} heads x first {T} of {cfg.T} tokens (B=1), "
-                       f"fp64 token loop, {passes} passes in {dt:.1f} s on {threads} threads; "
-                       f"rate scaled to {cfg.H} heads")
+                cpu_model=cpu_model(), host_cpus=os.cpu_count(),
+                sample=f"{heads} of {cfg.B * cfg.H} sequence-heads x first {T} of {cfg.T} "
+                       f"tokens, fp64 token loop, {passes} passes in {dt:.1f} s on {threads} "
+                       f"threads; rate scaled to all {cfg.B * cfg.H} sequence-heads")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "batched", "long"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long", choices=["prefill", "batched", "long"])
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other prefill configurations")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
@@ -423,19 +460,12 @@ def main():
     kda.load_library()
     cfg = W.PREFILL_CONFIGS[args.workload]
     steps = args.steps
-    if args.workload == "long":
-        steps = min(steps, 5)
     _log(f"[bench] prefill {cfg.describe()}: warmup {args.warmup}, steps {steps}")
     pre = bench_prefill(cfg, steps, args.warmup)
     _log(f"[bench] prefill kernel {pre['kernel_ms'] * 1e3:.1f} us, {pre['gbs']:.0f} GB/s, "
          f"{pre['tflops']:.1f} TFLOP/s")
 
     workload = cfg.describe()
-    traffic = measured_traffic("prefill", workload)
-    if pre["workspace_bytes"] > 0:
-        kernels = "prefill_prep_kernel + prefill_state_kernel"
-    else:
-        kernels = "prefill_fused_kernel"
     result = {
         "metric": "KDA prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW",
         "value": pre["tokens_per_s"],
@@ -452,15 +482,21 @@ def main():
         "config": {"workload": workload, "B": cfg.B, "T": cfg.T, "H": cfg.H, "dk": cfg.dk,
                    "dv": cfg.dv, "chunk": cfg.chunk, "state": "fp32",
                    "input_replicas": pre["replicas"], "workspace_bytes": pre["workspace_bytes"]},
-        "roofline": {"bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": pre["gbs"] / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": kernels,
-                     "kernel_us": pre["kernel_ms"] * 1e3, "algorithmic_bytes": pre["bytes"]},
-        "mfma": {"flops_per_step": pre["flops"], "achieved_tflops": pre["tflops"],
-                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": pre["tflops"] / MFMA_BF16_PEAK_TFLOPS,
-                 "frac_without_inverse": pre["tflops_cons"] / MFMA_BF16_PEAK_TFLOPS},
+        "roofline": prefill_roofline(pre, workload),
+        "mfma": prefill_mfma(pre),
     }
+
+    # the other bf16 prefill configurations, each with its own roofline
+    for key, name in (("prefill_4k", "prefill"), ("batched", "batched"), ("long", "long")):
+        if args.no_extra or name == args.workload:
+            continue
+        c = W.PREFILL_CONFIGS[name]
+        _log(f"[bench] {key}: {c.describe()}")
+        ex = bench_prefill(c, 20 if name != "long" else 5, 5 if name != "long" else 2)
+        _log(f"[bench] {key} {ex['kernel_ms'] * 1e3:.1f} us, {ex['gbs']:.0f} GB/s")
+        result[key] = {"workload": c.describe(), "us_per_call": ex["kernel_ms"] * 1e3,
+                       "tokens_per_s": ex["tokens_per_s"],
+                       "roofline": prefill_roofline(ex, c.describe()), "mfma": prefill_mfma(ex)}
 
     if not args.no_decode:
         dc = W.DECODE_CONFIGS["decode"]
@@ -493,7 +529,7 @@ def main():
 
     if not args.no_layer:
         _log("[bench] layer form (prologue + epilogue)")
-        ly = bench_layer(cfg)
+        ly = bench_layer(W.PREFILL_CONFIGS["prefill"])
         _log("[bench] layer " + ", ".join(
             f"{n} {ly[n]['us_per_call']:.1f} us" for n in ("plain", "bounded_l2_normgate",
                                                           "scalar_gate_l2")) +
@@ -503,7 +539,10 @@ def main():
 
     if not args.no_cpu:
         _log("[bench] cpu oracle baseline")
-        result["cpu_baseline"] = cpu_baseline_prefill(cfg, max_heads=os.cpu_count() or 1)
+        # the machine's CPU share (OMP_NUM_THREADS there), not the host's count
+        cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+                    or (os.cpu_count() or 1))
+        result["cpu_baseline"] = cpu_baseline_prefill(cfg, max_heads=cores)
 
     print(json.dumps(result), flush=True)
 

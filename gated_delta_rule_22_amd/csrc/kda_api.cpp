@@ -337,6 +337,11 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    // the matrix-core path's log-decay range is [-5, 0]: a wider bounded
+    // gate would be clamped there
+    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk) &&
+        (cfg.pro & 3) == KDA_GATE_BOUNDED && cfg.pr.bound > 5.f)
+        return KDA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return KDA_OK;
 
     const size_t elt = dtype == KDA_BF16 ? 2 : 4;

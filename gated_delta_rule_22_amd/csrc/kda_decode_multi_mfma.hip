@@ -16,8 +16,10 @@
 // permuted the same way on both operands. A committing pass then
 // adds K_restore^T U to each 16-row tile in fp32 on the matrix cores and
 // writes it back once; a verify pass (n = 0) only reads the state.
-// With T <= 8 and the log-decay bound of (-5, 0) per step, 1/a_t <= e^40 stays
-// inside fp32.
+// Each log-decay is clamped into [-10, 0], so 1/a_t <= e^80 stays inside
+// fp32 for any input. That holds the supported range (-5, 0) of the
+// trillion-scale architecture page, section 4, exactly; a step that decays
+// harder than exp(-10) keeps exp(-10) of the old state instead of less.
 #include <type_traits>
 
 #include "kda_common.h"
@@ -28,6 +30,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int TM = 8;             // most draft tokens
+constexpr float kLogDecayFloor = -10.f;   // TM * 10 = 80 < 88 (fp32 exp range)
 constexpr int AS = D + 8;         // bf16 row stride of [16][D] operand tiles
 constexpr int RS = 16 + 8;        // bf16 row stride of K_restore^T [D][16 token slots]
 
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(256, 4) void decode_multi_mfma_kernel(
         float cum[TM];
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            if (t < T) c += la_t[t];
+            if (t < T) c += __builtin_amdgcn_fmed3f(la_t[t], kLogDecayFloor, 0.f);
             cum[t] = c;
             if (t + 1 == n) cn = c;
         }

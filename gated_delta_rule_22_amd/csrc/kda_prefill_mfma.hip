@@ -58,6 +58,13 @@ constexpr int LDT = 16 * 16 + 4;   // fp32 stride of one diagonal L block
 // channel uses the chunk-level decay reference (1/a <= exp(8 * kRangeDecay)).
 constexpr float kRangeDecay = 8.f;
 constexpr float kLog2e = 1.4426950408889634f;
+// Per-step log-decays are clamped into [-5, 0], the supported range (the
+// bound on the trillion-scale architecture page, section 4; a decay never
+// exceeds 1). A 16-token block then needs 1/b <= exp(80), inside fp32 and
+// bf16, so every input gives finite results; a step that decays harder than
+// exp(-5) keeps exp(-5) of the old state instead of less (within about 0.7%
+// of the exact step for that channel).
+constexpr float kLogDecayFloor = -5.f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -212,6 +219,14 @@ __device__ __forceinline__ void prologue(Prep& sm, Inputs<NW>& in, const Prologu
             const f32x2 g = unpack2(__builtin_bit_cast(u32x2, in.la[j])[0]);   // raw gate bits in .x
             in.la[j] = f32x2{-pr.bound * sigmoid_f(g[0]), -pr.bound * sigmoid_f(g[1])};
         }
+    }
+    // (the host rejects a bounded gate past the floor: that form is always
+    // inside the range)
+    if constexpr ((PRO & 3) != kGateBounded) {
+#pragma unroll
+        for (int j = 0; j < TPT; ++j)
+            in.la[j] = f32x2{__builtin_amdgcn_fmed3f(in.la[j][0], kLogDecayFloor, 0.f),
+                             __builtin_amdgcn_fmed3f(in.la[j][1], kLogDecayFloor, 0.f)};
     }
     if constexpr ((PRO & kProL2) != 0) {
         // squared norms by packed bf16 dot products (v_dot2: no unpacked
@@ -1008,14 +1023,18 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         }
         if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
-        // 54 A operands, 16 B per lane each, all stored during the
-        // substitution so that the stores overlap its matrix work: the 38
-        // that are final before it (Q_decay, M_qk, K_restore^T) five per
-        // wave, one or two after each block (waves 6, 7 store their fifth
-        // twice: same data, same address), and -W straight from the
-        // registers that form it, each wave its 8-byte half of the four
-        // operands of its channel tile. Every wave thus issues a fixed
-        // number of stores.
+        // Operand record stores (16 B per lane per A operand), each placed
+        // where it overlaps other work:
+        //   K_restore^T (16): waves 6-7, during stage 2 (above);
+        //   Q_decay (16): waves 4-7, during stage 2 on the chunk reference
+        //     (above), else after the substitution's block 0 (below);
+        //   M_qk (6): waves 0-5, one each, after block 0 (below);
+        //   -W (16): every wave, straight from the registers that form it in
+        //     the substitution, its 8-byte half of the four operands of its
+        //     channel tile;
+        //   a_last and U0: from registers after the substitution.
+        // Which stores a wave issues depends only on its index and the
+        // chunk's decay reference, both wave-uniform.
         auto early = [&](int I) {
             // M_qk: one operand each for waves 0-5 after block 0
             if (I == 0 && wave < 6)

@@ -33,7 +33,13 @@
  * Supported on the GPU: dk, dv in {16, 32, 64, 128}; chunk in {0 (=64), 16,
  * 32, 64}; dtype fp32 or bf16. All device pointers must be 16-byte aligned.
  * The log-decay is meant to lie in [-5, 0] per step (the bound stated on the
- * trillion-scale page, section 4); results stay finite for that range.
+ * trillion-scale page, section 4). The fp32 paths take any value exactly.
+ * The bf16 matrix-core paths clamp each log-decay first, so their results
+ * are finite for every input: the prefill (dk = dv = 128, chunk 64) into
+ * [-5, 0], kda_decode_multi drafts of 2..8 tokens into [-10, 0]. A step that
+ * decays harder than the floor keeps exp(floor) of the old state (0.7% for
+ * the prefill) instead of less; its error is that fraction of the old
+ * state's contribution.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -200,7 +206,10 @@ typedef enum {
 
 typedef struct {
     kda_gate gate;
-    float decay_bound;         /* KDA_GATE_BOUNDED; 0 selects 5 */
+    float decay_bound;         /* KDA_GATE_BOUNDED; 0 selects 5. Above 5 is
+                                  KDA_ERR_UNSUPPORTED on the bf16 matrix-core
+                                  prefill (bf16, dk = dv = 128, chunk 64), whose
+                                  log-decay range is [-5, 0] */
     int l2norm_qk;             /* nonzero: q, k arrive raw and are divided by
                                   sqrt(sum of squares + l2_eps) per token and head */
     float l2_eps;              /* 0 selects 1e-6 */

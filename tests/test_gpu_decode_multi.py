@@ -68,6 +68,24 @@ def test_multi_bf16_random_accept():
     report(f"multi bf16 B{B} H{H} T{T} n={n}", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
+def test_multi_bf16_decay_past_the_bound():
+    # Log-decays of -8 to -20 per step on some channels and tokens, outside
+    # the supported [-5, 0]: the matrix-core draft kernel clamps them to -10
+    # (keeping exp(-10) of the old state), so it stays finite and within the
+    # bf16 tolerance of the exact recurrence.
+    B, T, H = 4, 8, 8
+    x = inputs(B, T, H, seed=23)
+    g = torch.Generator().manual_seed(24)
+    x["log_alpha"][:, :, :, :16] = -8.0 - 12.0 * torch.rand(B, T, H, 16, generator=g)
+    x["log_alpha"][:, 5] = -8.0 - 12.0 * torch.rand(B, H, 128, generator=g)
+    n = [8, 3, 0, 6]
+    o, S = gpu_multi(x, n)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    ro, rS = oracle_multi(x, n)
+    report(f"multi bf16 log-decay -8..-20 B{B} H{H} T{T} n={n}", [("o", o, ro), ("S", S, rS)],
+           TOL_BF16)
+
+
 def test_verify_leaves_state_untouched():
     x = inputs(4, 6, 8, seed=31)
     o, S = gpu_multi(x, [0, 0, 0, 0])

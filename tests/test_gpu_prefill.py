@@ -118,53 +118,113 @@ def test_bf16_batched_config_sampled():
                [("o", o[b:b + 1, :, h:h + 1], ro), ("S", S[b:b + 1, h:h + 1], rS)], TOL_BF16)
 
 
-def test_bf16_long_config_sampled():
+@pytest.fixture(scope="module")
+def long_case():
+    """The 1M-token configuration at full size, built head by head from the
+    per-head seeds, and one prefill call on it (the benchmark's launch
+    configuration)."""
+    c = W.PREFILL_CONFIGS["long"]
+    x = W.prefill_inputs_by_head(c, device=DEV)
+    o, S = kda.kda_prefill_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None)
+    torch.cuda.synchronize()
+    yield dict(q=x["q"], k=x["k"], v=x["v"], la=x["log_alpha"], beta=x["beta"], o=o, S=S,
+               T=c.T)
+    del x, o, S
+    torch.cuda.empty_cache()
+
+
+def _window_from_zero(x, h, a, Wn):
+    """Oracle outputs of head h on tokens [a, a + Wn) from a zero state, and
+    the damping bound of the history: the product of the largest per-step
+    decay over the first half of the window (outputs are compared only in
+    the second half, where the true history is damped by at least that)."""
+    win = slice(a, a + Wn)
+    head = lambda t: t[:, win, h:h + 1].cpu()
+    lmax = x["la"][0, win, h].double().max(dim=-1).values
+    damp_o = float(torch.exp(lmax[:Wn // 2].sum()))
+    damp_s = float(torch.exp(lmax.sum()))
+    ro, rS = oracle.prefill_f64(head(x["q"]), head(x["k"]), head(x["v"]), head(x["la"]),
+                                head(x["beta"]), None)
+    return ro, rS, damp_o, damp_s
+
+
+def test_bf16_long_config_sampled(long_case):
     """1M-token context at full size. Sampled heads are checked on the first
     65536 tokens exactly, and at the end against a run of the last 65536
     tokens from a zero state: the state entering that window is damped by the
     product of the largest per-step decay over the window, which the test
     computes and requires to be negligible against the tolerance (outputs are
     compared only in the second half of the window, where the same holds)."""
-    c = W.PREFILL_CONFIGS["long"]
-    T, H, D = c.T, c.H, c.dk
-    q = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=DEV)
-    k = torch.empty_like(q)
-    v = torch.empty_like(q)
-    la = torch.empty((1, T, H, D), dtype=torch.float32, device=DEV)
-    beta = torch.empty((1, T, H), dtype=torch.float32, device=DEV)
-    for h in range(H):
-        xh = W.prefill_inputs_per_head(c, h, device=DEV)
-        q[:, :, h] = xh["q"][:, :, 0]
-        k[:, :, h] = xh["k"][:, :, 0]
-        v[:, :, h] = xh["v"][:, :, 0]
-        la[:, :, h] = xh["log_alpha"][:, :, 0]
-        beta[:, :, h] = xh["beta"][:, :, 0]
-        del xh
-    o, S = kda.kda_prefill_fwd(q, k, v, la, beta, None)
-    torch.cuda.synchronize()
+    x = long_case
+    T, o, S = x["T"], x["o"], x["S"]
     Wn = 65536
+    skip = Wn // 2
     for h in (0, 21):
-        head = lambda t, sl: t[:, sl, h:h + 1].cpu()
         first = slice(0, Wn)
-        ro, _ = oracle.prefill_f64(head(q, first), head(k, first), head(v, first),
-                                   head(la, first), head(beta, first), None)
+        head = lambda t: t[:, first, h:h + 1].cpu()
+        ro, _ = oracle.prefill_f64(head(x["q"]), head(x["k"]), head(x["v"]), head(x["la"]),
+                                   head(x["beta"]), None)
         report(f"long config first {Wn} tokens, head {h}", [("o", o[:, first, h:h + 1], ro)],
                TOL_BF16)
-        # Window from a zero state: the history entering it is damped by the
-        # product of the largest per-step decay over the tokens before the
-        # compared position. Outputs are compared only past `skip` tokens.
-        last = slice(T - Wn, T)
-        skip = Wn // 2
-        lmax = la[0, last, h].double().max(dim=-1).values
-        damp_o = float(torch.exp(lmax[:skip].sum()))
-        damp_s = float(torch.exp(lmax.sum()))
+        ro, rS, damp_o, damp_s = _window_from_zero(x, h, T - Wn, Wn)
         assert damp_o < 1e-6 and damp_s < 1e-6, (damp_o, damp_s)
-        ro, rS = oracle.prefill_f64(head(q, last), head(k, last), head(v, last),
-                                    head(la, last), head(beta, last), None)
         report(f"long config last {Wn - skip} tokens + final state, head {h} "
                f"(damping {damp_o:.1e} / {damp_s:.1e})",
                [("o", o[:, T - Wn + skip:, h:h + 1], ro[:, skip:]), ("S", S[:, h:h + 1], rS)],
                TOL_BF16)
+
+
+def test_bf16_long_config_mid_window(long_case):
+    """The same 1M-token call, a window in the middle of the sequence (tokens
+    524,288 .. 589,824) on head 11, against the oracle run from a zero state
+    at the window start, under the same damping bound."""
+    x = long_case
+    h, a, Wn = 11, x["T"] // 2, 65536
+    skip = Wn // 2
+    ro, _, damp_o, _ = _window_from_zero(x, h, a, Wn)
+    assert damp_o < 1e-6, damp_o
+    report(f"long config tokens {a + skip}..{a + Wn}, head {h} (damping {damp_o:.1e})",
+           [("o", x["o"][:, a + skip:a + Wn, h:h + 1], ro[:, skip:])], TOL_BF16)
+
+
+def test_split_path_regimes_alternate_within_workgroup():
+    # Few heads with enough chunks that each prep workgroup takes several in
+    # a row (B1 H2 T32768: 4 chunks per workgroup), with a strongly decaying
+    # channel in every other chunk: the workgroup alternates between the
+    # chunk-level decay reference and the 16-token block factorisation.
+    c = W.PREFILL_CONFIGS["prefill"]
+    T = 32768
+    x = W.prefill_inputs(c, B=1, T=T, H=2)
+    for ch in range(1, T // 64, 2):
+        x["log_alpha"][:, ch * 64 + 8:ch * 64 + 16, :, (3 * ch) % 128] = -1.5   # e^-12 over 8 tokens
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report("split path, regimes alternating per chunk, B1 H2 T32768",
+           [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+@pytest.mark.parametrize("B,H", [(1, 2), (2, 64), (4, 64)])   # split, fused 64- and 128-column
+def test_decay_past_the_bound_stays_finite(B, H):
+    # Log-decays of -8 to -20 per step, outside the supported [-5, 0]: on
+    # one channel over whole 16-token blocks, and on every channel for a few
+    # tokens. The matrix-core path clamps them to -5 (keeping exp(-5) of the
+    # old state instead of less), so its results stay finite and within the
+    # bf16 tolerance of the exact recurrence.
+    c = W.PREFILL_CONFIGS["prefill"]
+    x = W.prefill_inputs(c, B=B, T=200, H=H)
+    g = torch.Generator().manual_seed(5)
+    deep = lambda shape: -8.0 - 12.0 * torch.rand(shape, generator=g)
+    x["log_alpha"][:, 16:48, :, 9] = deep(x["log_alpha"][:, 16:48, :, 9].shape)
+    x["log_alpha"][:, 130:134] = deep(x["log_alpha"][:, 130:134].shape)
+    o, S = gpu_prefill(to_dev(x))
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    if B * H > 8:   # oracle on a few heads
+        idx = [0, H // 2, H - 1]
+        x = {k: (None if v is None else v[:1, :, idx] if k != "S0" else v[:1, idx])
+             for k, v in x.items()}
+        o, S = o[:1, :, idx], S[:1, idx]
+    ro, rS = oracle_prefill(x)
+    report(f"log-decay -8..-20 B{B} H{H} T200", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])

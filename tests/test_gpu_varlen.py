@@ -15,7 +15,7 @@ import torch
 import gated_delta_rule_22_amd as kda
 import oracle
 import workloads as W
-from gpu_helpers import DEV, TOL_BF16, TOL_F32, report, to_dev
+from gpu_helpers import per_head_rel_l2, DEV, TOL_BF16, TOL_F32, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,8 @@ def check(label, x, got, ref, tol):
         if b > a:
             e = oracle.rel_l2(o[a:b].cpu(), ro[a:b])
             assert e <= tol, f"{label}: sequence {i} o rel-L2 {e:.3e}"
+            e, h = per_head_rel_l2(o[a:b].cpu(), ro[a:b], (1,))
+            assert e <= tol, f"{label}: sequence {i} head {h} o rel-L2 {e:.3e}"
         e = oracle.rel_l2(S[i].cpu(), rS[i])
         assert e <= tol, f"{label}: sequence {i} S_final rel-L2 {e:.3e}"
 
@@ -171,7 +173,7 @@ def test_varlen_config_full_size_sampled():
         sub["S0"] = x["S0"][i:i + 1]
         sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32)
         ro, rS, rSc = run_oracle(sub, c.ckpt_every)
-        pairs = [("o", o[a:b], ro), ("S_final", S[i:i + 1], rS)]
+        pairs = [("o", o[a:b], ro, (1,)), ("S_final", S[i:i + 1], rS)]
         if rSc.shape[0]:
             pairs.append(("S_ckpt", Sc[ck0[i]:ck0[i + 1]], rSc))
         report(f"varlen full size: sequence {i} ({b - a} tokens, all heads)", pairs, TOL_BF16)

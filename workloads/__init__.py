@@ -30,7 +30,8 @@ import torch
 
 __all__ = [
     "PrefillConfig", "DecodeConfig", "PREFILL_CONFIGS", "DECODE_CONFIGS",
-    "prefill_inputs", "prefill_inputs_per_head", "decode_state", "decode_step_inputs",
+    "prefill_inputs", "prefill_inputs_per_head", "prefill_inputs_by_head", "decode_state",
+    "decode_step_inputs",
     "VarlenConfig", "VARLEN_CONFIGS", "varlen_lengths", "varlen_inputs", "layer_inputs",
 ]
 
@@ -157,6 +158,26 @@ def prefill_inputs_per_head(cfg: PrefillConfig, h: int, *, T: Optional[int] = No
     context can be built head by head and any head regenerated alone.
     Shapes are [1, T, 1, d] / [1, T, 1] / [1, 1, dk, dv]."""
     return prefill_inputs(cfg, B=1, T=T, H=1, seed=cfg.seed + h, device=device, dtype=dtype)
+
+
+def prefill_inputs_by_head(cfg: PrefillConfig, *, T: Optional[int] = None, device="cpu") -> dict:
+    """A single-sequence batch (B = 1) assembled from per-head draws
+    (prefill_inputs_per_head for h = 0..H-1), so that any head of a long
+    context can later be regenerated alone. Shapes as prefill_inputs."""
+    assert cfg.B == 1 and cfg.s0_std == 0, "per-head draws are defined for B = 1, S0 = 0"
+    T = cfg.T if T is None else T
+    H, dk, dv = cfg.H, cfg.dk, cfg.dv
+    out = dict(q=torch.empty((1, T, H, dk), dtype=cfg.dtype, device=device),
+               k=torch.empty((1, T, H, dk), dtype=cfg.dtype, device=device),
+               v=torch.empty((1, T, H, dv), dtype=cfg.dtype, device=device),
+               log_alpha=torch.empty((1, T, H, dk), dtype=torch.float32, device=device),
+               beta=torch.empty((1, T, H), dtype=torch.float32, device=device), S0=None)
+    for h in range(H):
+        xh = prefill_inputs_per_head(cfg, h, T=T, device=device)
+        for n in ("q", "k", "v", "log_alpha", "beta"):
+            out[n][:, :, h] = xh[n][:, :, 0]
+        del xh
+    return out
 
 
 def decode_state(cfg: DecodeConfig, device="cpu") -> torch.Tensor:

@@ -20,6 +20,7 @@ __all__ = [
     "kda_prefill_workspace_size", "kda_prefill_fwd", "kda_prefill_varlen_workspace_size",
     "kda_prefill_varlen", "kda_decode_step", "kda_decode_multi", "kda_prefill_layer",
     "kda_decode_layer", "KDA_GATE_LOG", "KDA_GATE_BOUNDED", "KDA_GATE_SCALAR",
+    "kda_prefill_fwd_noalloc", "KDA_NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +82,9 @@ def load_library():
     lib.kda_decode_step.restype = i
     lib.kda_decode_multi.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, vp]
     lib.kda_decode_multi.restype = i
+    lib.kda_prefill_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, i, i,
+                                            vp]
+    lib.kda_prefill_fwd_noalloc.restype = i
     _lib = lib
     return lib
 
@@ -155,6 +159,43 @@ def kda_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != 0:
         raise KDAError(st, "kda_prefill_fwd")
     return o, S_final
+
+
+KDA_NOALLOC_SCRATCH_BYTES = 80 << 20   # include/kda.h
+
+
+def kda_prefill_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            log_alpha: torch.Tensor, beta: torch.Tensor,
+                            S0: Optional[torch.Tensor], o: torch.Tensor,
+                            S_final: Optional[torch.Tensor], *, chunk: int = 64,
+                            stream=None) -> None:
+    """kda_prefill_fwd through the entry point that allocates nothing: the
+    caller passes the outputs, and the library's static device scratch serves
+    as the workspace. Layouts as kda_prefill_fwd."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda_prefill_fwd_noalloc needs GPU tensors")
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check(q, "q", (B, T, H, dk), dt, dev)
+    _check(k, "k", (B, T, H, dk), dt, dev)
+    _check(v, "v", (B, T, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, T, H, dk), torch.float32, dev)
+    _check(beta, "beta", (B, T, H), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    _check(o, "o", (B, T, H, dv), dt, dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    st = lib.kda_prefill_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                     _ptr(S0), _ptr(o), _ptr(S_final), B, T, H, dk, dv,
+                                     _DTYPES[dt], chunk, _stream(stream, dev))
+    if st != 0:
+        raise KDAError(st, "kda_prefill_fwd_noalloc")
 
 
 def kda_prefill_varlen_workspace_size(N: int, T_total: int, H: int, dk: int, dv: int,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <cstring>
+#include <mutex>
 
 #include "kda_launch.h"
 
@@ -53,6 +54,9 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
         case KDA_ERR_WORKSPACE: return "workspace missing or too small";
         case KDA_ERR_HIP: return "HIP launch failed";
+        case KDA_ERR_SCRATCH:
+            return "the call needs more device scratch than the library's static buffer "
+                   "holds (kda_prefill_fwd_noalloc; use kda_prefill_fwd with a workspace)";
     }
     return "unknown status";
 }
@@ -443,6 +447,61 @@ kda_status kda_decode_layer(const void* q, const void* k, const void* v, const v
     a.out_eps = cfg.out_eps;
     const hipError_t e = kda::launch_decode(dtype == KDA_BF16, dk, dv, a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+
+// ---------------------------------------------------------------------------
+// Prefill without any allocation: the workspace of kda_prefill_fwd lives in a
+// file-scope device array instead of a caller buffer. Each GPU the library
+// runs on holds its own copy (KDA_NOALLOC_SCRATCH_BYTES) until the process
+// ends. The host-side name `scratch` only stands in for that memory: its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is ever passed to a kernel.
+
+}  // extern "C"
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (null on failure).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta,
+                                   const float* S0, void* o, float* S_final,
+                                   int B, int T, int H, int dk, int dv,
+                                   kda_dtype dtype, int chunk, void* stream) {
+    const size_t need = kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk);
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_for_current_device();
+        if (!ws) return KDA_ERR_HIP;
+    }
+    // every other rule (and every launch) is kda_prefill_fwd's; its kernels
+    // write each record of the workspace before they read it, so the array
+    // needs no clearing between calls
+    return kda_prefill_fwd(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, dk, dv, dtype,
+                           chunk, ws, need > 0 ? KDA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 }  // extern "C"

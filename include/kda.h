@@ -55,7 +55,9 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment, aliasing */
     KDA_ERR_UNSUPPORTED = 2,   /* dk, dv, chunk or dtype outside the supported set */
     KDA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-    KDA_ERR_HIP = 4            /* a HIP call or kernel launch failed */
+    KDA_ERR_HIP = 4,           /* a HIP call or kernel launch failed */
+    KDA_ERR_SCRATCH = 5        /* kda_prefill_fwd_noalloc: the call needs more than
+                                  the static scratch buffer holds */
 } kda_status;
 
 typedef enum {
@@ -242,6 +244,27 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
 kda_status kda_decode_layer(const void* q, const void* k, const void* v, const void* gate,
                             const float* beta, float* S, void* o, int B, int H, int dk, int dv,
                             kda_dtype dtype, const kda_layer_opts* opts, void* stream);
+
+/*
+ * kda_prefill_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, which instead lives in a static
+ * device array inside the library, KDA_NOALLOC_SCRATCH_BYTES (80 MiB) on each
+ * GPU the library runs on, held until the process ends. Calls that need more
+ * (kda_prefill_workspace_size() above that) return KDA_ERR_SCRATCH and launch
+ * nothing; 16 heads of 4096 tokens need 73.9 MB. The call itself allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.
+ * Every call on one GPU shares that GPU's array, and it keeps the last
+ * call's contents: calls that overlap on one GPU (on different streams, or
+ * from different host threads without ordering) race and must be avoided.
+ * Calls ordered on one stream are safe.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+kda_status kda_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta,
+                                   const float* S0, void* o, float* S_final,
+                                   int B, int T, int H, int dk, int dv,
+                                   kda_dtype dtype, int chunk, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* kda_status_string(kda_status status);

@@ -11,7 +11,7 @@ import gated_delta_rule_22_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, 1, 2, 3, 4, 5
 
 
 @pytest.fixture(scope="module")
@@ -33,13 +33,14 @@ def test_exports_every_declared_symbol(lib):
     assert set(syms) == {"kda_prefill_workspace_size", "kda_prefill_fwd",
                          "kda_prefill_varlen_workspace_size", "kda_prefill_varlen",
                          "kda_prefill_layer", "kda_decode_layer",
-                         "kda_decode_step", "kda_decode_multi", "kda_status_string"}
+                         "kda_decode_step", "kda_decode_multi", "kda_status_string",
+                         "kda_prefill_fwd_noalloc"}
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_status_strings(lib):
-    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, 99):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH, 99):
         assert kda.kda_status_string(code)
     assert kda.kda_status_string(OK) == "ok"
 

@@ -65,8 +65,7 @@ size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype
                                   int chunk) {
     if (B <= 0 || T <= 0 || H <= 0 || dtype != KDA_BF16) return 0;
     if (!kda::prefill_mfma_supported(dk, dv, chunk)) return 0;
-    const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
-    return kda::prefill_mfma_workspace((long)B * H, nch, H);
+    return kda::prefill_mfma_workspace_fixed(B, H, ((long)T + kChunk - 1) / kChunk);
 }
 
 kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
@@ -119,7 +118,7 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
 
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    const kda::SeqLayout sq{nullptr, B, T, kChunk, 0};
+    const kda::SeqLayout sq{nullptr, B, T, kChunk, 0, T};
     if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
         const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
         if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
@@ -211,7 +210,7 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
     int* tab = (int*)ws;
     hipError_t e = kda::launch_varlen_table(cu_seqlens, N, T_total, kChunk, ckpt_every, tab, st);
     if (e != hipSuccess) return KDA_ERR_HIP;
-    const kda::SeqLayout sq{tab, N, T_total, kChunk, ckpt_every};
+    const kda::SeqLayout sq{tab, N, T_total, kChunk, ckpt_every, T_total};
     // With no tokens every sequence is empty and only S_final = S0 remains:
     // the generic kernel does that without touching a chunk record.
     bool epi_done;
@@ -387,7 +386,7 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
     if (overlap(ro, rsf) || overlap(ro, rws) || overlap(rsf, rws)) return KDA_ERR_INVALID_ARG;
 
     hipStream_t st = (hipStream_t)stream;
-    const kda::SeqLayout sq{nullptr, B, T, kChunk, 0};
+    const kda::SeqLayout sq{nullptr, B, T, kChunk, 0, T};
     hipError_t e;
     bool epi_done = false;
     if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {

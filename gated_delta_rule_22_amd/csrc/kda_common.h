@@ -78,13 +78,16 @@ __device__ __forceinline__ int wave_id() {
 //   tab[2N+2 .. 3N+2]     first checkpoint slot of each sequence
 // K is the checkpoint interval in tokens (a multiple of C), 0 for none:
 // sequence i has len(i) / K checkpoints, the states after K, 2K, ... tokens.
+// Without a table, sequence i starts at token i * S (S >= T: a window of T
+// tokens of longer sequences, as the piecewise prefill walks them).
 struct SeqLayout {
     const int* tab;
     int N;   // sequences
     int T;   // tokens per sequence (no table) or in all (table)
     int C;   // chunk length of the chunk numbering
     int K;   // checkpoint interval, 0 = none
-    __device__ long start(int i) const { return tab ? (long)tab[i] : (long)i * T; }
+    long S;  // tokens between sequence starts (no table)
+    __device__ long start(int i) const { return tab ? (long)tab[i] : (long)i * S; }
     __device__ int len(int i) const { return tab ? tab[i + 1] - tab[i] : T; }
     __device__ long chunk0(int i) const {
         return tab ? (long)tab[N + 1 + i] : (long)i * ((T + C - 1) / C);

@@ -62,6 +62,12 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
 bool prefill_mfma_supported(int dk, int dv, int chunk);
 bool prefill_mfma_split(long pairs);
 size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H);
+// Fixed-length batches (B sequences of nch_seq chunks): the workspace of the
+// split path, which for long sequences holds one piece of records (the
+// launcher then walks the sequence piece by piece) plus a carried state.
+size_t prefill_mfma_workspace_fixed(int B, int H, long nch_seq);
+// Chunks per sequence of one piece of the piecewise split path, 0 = none.
+long prefill_mfma_piece(long pairs, long nch_seq);
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* gate,
                                const float* beta, const float* S0, void* o, float* S_final,
                                const SeqLayout& sq, int H, int nch_all, void* ws,

@@ -41,6 +41,7 @@
 //    passes, twelve waves per 16 value columns: four compute U, four
 //    update the state, four form the output rows; each loads only its
 //    operands, straight into MFMA registers, while the other passes run.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_common.h"
@@ -930,7 +931,7 @@ struct ChunkMap {
     __device__ ChunkPos at(int gc) const {
         if (!kTable) {
             const int i = gc / nch;
-            return {(long)i * sq.T, sq.T, gc - i * nch};
+            return {sq.start(i), sq.T, gc - i * nch};
         }
         // the sequence is the last entry whose first chunk is <= gc
         const int i = __builtin_popcountll(__builtin_amdgcn_ballot_w64(cst[0] <= gc)) +
@@ -942,7 +943,7 @@ struct ChunkMap {
     __device__ ChunkPos next(const ChunkPos& p, int gc) const {
         if (!kTable) {
             if (p.c + 1 < nch) return {p.tok0, p.len, p.c + 1};
-            return {p.tok0 + sq.T, p.len, 0};
+            return {p.tok0 + sq.S, p.len, 0};
         }
         return at(gc + 1);
     }
@@ -1318,7 +1319,20 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
 
 // ---------------------------------------------------------------------------
 namespace {
+constexpr size_t DK_STATE_BYTES = size_t(128) * 128 * 4;   // one fp32 state
+}
+
+#ifndef KDA_PIECE_CHUNKS
+#define KDA_PIECE_CHUNKS 48
+#endif
+namespace {
 constexpr long kSplitBelowHeads = 128;   // fewer heads than this: prep + state kernels
+// Piecewise split path: fixed-length batches whose records would outgrow the
+// last-level cache run prep and state walk piece by piece along the
+// sequence, KDA_PIECE_CHUNKS chunks per sequence at a time (more when the
+// batch has few sequence-heads, so that a piece's prep still covers the GPU).
+constexpr size_t kPieceAbove = size_t(192) << 20;
+constexpr long kPieceMinWork = 512;      // chunk-heads per piece, at least
 }
 
 bool prefill_mfma_supported(int dk, int dv, int chunk) {
@@ -1330,6 +1344,23 @@ bool prefill_mfma_split(long pairs) { return pairs < kSplitBelowHeads; }
 size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H) {
     if (!prefill_mfma_split(pairs)) return 0;
     return (size_t)H * nch_all * mf::REC_BYTES;
+}
+
+long prefill_mfma_piece(long pairs, long nch_seq) {
+    if (!prefill_mfma_split(pairs)) return 0;
+    if ((size_t)pairs * (size_t)nch_seq * mf::REC_BYTES <= kPieceAbove) return 0;
+    long L = KDA_PIECE_CHUNKS;
+    while (L * pairs < kPieceMinWork) L *= 2;
+    return L < nch_seq ? L : 0;
+}
+
+size_t prefill_mfma_workspace_fixed(int B, int H, long nch_seq) {
+    const long pairs = (long)B * H;
+    const long L = prefill_mfma_piece(pairs, nch_seq);
+    if (L == 0) return prefill_mfma_workspace(pairs, (size_t)B * (size_t)nch_seq, H);
+    // one piece of records, then the carried state (used when the caller
+    // wants no S_final)
+    return (size_t)pairs * (size_t)L * mf::REC_BYTES + (size_t)pairs * DK_STATE_BYTES;
 }
 
 namespace {
@@ -1345,6 +1376,59 @@ auto fused_kernel_for(bool ck, bool epi) {
         return ck ? prefill_fused_kernel<NW, true, 0> : prefill_fused_kernel<NW, false, 0>;
     else
         return prefill_fused_kernel<NW, false, PRO>;
+}
+
+// Piecewise split path (fixed-length batch, sq.tab == nullptr): for each
+// piece of L chunks of every sequence, the prep kernel writes its records
+// (one piece of the workspace, reused) and the state kernel walks them,
+// reading the state the previous piece left in `carry` (S_final, or the
+// state buffer after the records when the caller wants none). Records are
+// read back while they are still in the last-level cache.
+template <int PRO>
+hipError_t launch_mfma_pieces(const void* q, const void* k, const void* v, const void* gate,
+                              const float* beta, const float* S0, void* o, float* S_final,
+                              const SeqLayout& sq, int H, int nch_all, void* ws, long L,
+                              const Prologue& pr, hipStream_t st)
+{
+    constexpr int GM = PRO & 3;
+    const int B = sq.N;
+    const long pairs = (long)B * H;
+    const long nch_seq = nch_all / B;
+    char* rec = (char*)ws;
+    float* carry = S_final ? S_final : (float*)(rec + (size_t)pairs * L * mf::REC_BYTES);
+    const size_t ws_piece = (size_t)pairs * L * mf::REC_BYTES;
+    const unsigned threads = ws_piece > (size_t(128) << 20) ? 832u : 768u;
+    const long groups = (pairs + 7) / 8;
+    for (long c0 = 0; c0 < nch_seq; c0 += L) {
+        const long Lc = std::min(L, nch_seq - c0);
+        const long t0 = c0 * mf::C;
+        const int Tp = (int)std::min(Lc * mf::C, (long)sq.T - t0);
+        const SeqLayout sp{nullptr, B, Tp, mf::C, 0, sq.S};
+        const size_t row = (size_t)t0 * H;        // first (token, head) row of the piece
+        const bf16* qp = (const bf16*)q + row * mf::DK;
+        const bf16* kp = (const bf16*)k + row * mf::DK;
+        const bf16* vp = (const bf16*)v + row * 128;
+        const float* bp = beta + row;
+        const void* gp = GM == kGateLog ? (const void*)((const float*)gate + row * mf::DK)
+                       : GM == kGateBounded ? (const void*)((const bf16*)gate + row * mf::DK)
+                       : (const void*)((const float*)gate + row);
+        bf16* op = (bf16*)o + row * 128;
+        const int nch_piece = (int)(B * Lc);
+        const long work = (long)H * nch_piece;
+        int cpw = (int)((work + 255) / 256);
+        if (cpw < 1) cpw = 1;
+        const long ngrp = (nch_piece + cpw - 1) / cpw;
+        hipLaunchKernelGGL((prefill_prep_kernel<false, PRO>), dim3((unsigned)(H * ngrp)), dim3(512),
+                           0, st, qp, kp, vp, gp, bp, rec, sp, H, cpw, nch_piece, pr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(prefill_state_kernel<false>, dim3((unsigned)(groups * 64)), dim3(threads),
+                           0, st, (const char*)rec, c0 == 0 ? S0 : (const float*)carry, op, carry,
+                           sp, H, (int)pairs, nch_piece, (float*)nullptr, 0);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int PRO>
@@ -1369,6 +1453,10 @@ hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const vo
         *epi_done = epi;
         return hipGetLastError();
     }
+    // few sequence-heads, long sequences: prep and state walk piece by piece
+    const long L = sq.tab ? 0 : prefill_mfma_piece(pairs, (long)nch_all / sq.N);
+    if (L > 0) return launch_mfma_pieces<PRO>(q, k, v, gate, beta, S0, o, S_final, sq, H,
+                                              nch_all, ws, L, pr, st);
     // few sequence-heads: chunk-parallel prep, then the state walk
     if (nch_all > 0) {
         const long work = (long)H * nch_all;

@@ -203,6 +203,40 @@ def test_split_path_regimes_alternate_within_workgroup():
            [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
+def test_piecewise_split_path_all_heads():
+    # Few heads with records that would outgrow the last-level cache: the
+    # split path runs prep and state walk piece by piece along the sequence
+    # (B1 H4 T65536: eight pieces of 128 chunks), the state carried in S_final.
+    c = W.PREFILL_CONFIGS["long"]
+    x = W.prefill_inputs(c, B=1, T=65536, H=4, seed=31)
+    assert kda.kda_prefill_workspace_size(1, 65536, 4, 128, 128, torch.bfloat16) < 64 << 20
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report("piecewise split path B1 H4 T65536", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
+@pytest.mark.parametrize("mode", ["S_final", "no_state", "in_place"])
+def test_piecewise_split_path_batch_ragged(mode):
+    # Two sequences (strided windows of the batch), a carried S0 and a ragged
+    # last piece of one chunk of 33 tokens; the state carried in S_final, in
+    # the workspace (no S_final wanted), or in S0 itself (S_final = S0).
+    c = W.PREFILL_CONFIGS["batched"]
+    T = 49152 + 33
+    x = W.prefill_inputs(c, B=2, T=T, H=2, seed=32)
+    xd = to_dev(x)
+    if mode == "S_final":
+        o, S = gpu_prefill(xd)
+    elif mode == "no_state":
+        o, S = gpu_prefill(xd, want_state=False)
+        assert S is None
+    else:
+        S_io = xd["S0"].clone()
+        o, S = gpu_prefill(xd, S0=S_io, S_final=S_io)
+    ro, rS = oracle_prefill(x)
+    pairs = [("o", o, ro)] + ([("S", S, rS)] if S is not None else [])
+    report(f"piecewise split path B2 H2 T{T} ({mode})", pairs, TOL_BF16)
+
+
 @pytest.mark.parametrize("B,H", [(1, 2), (2, 64), (4, 64)])   # split, fused 64- and 128-column
 def test_decay_past_the_bound_stays_finite(B, H):
     # Log-decays of -8 to -20 per step, outside the supported [-5, 0]: on

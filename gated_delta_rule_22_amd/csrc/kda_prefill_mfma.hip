@@ -1323,7 +1323,7 @@ constexpr size_t DK_STATE_BYTES = size_t(128) * 128 * 4;   // one fp32 state
 }
 
 #ifndef KDA_PIECE_CHUNKS
-#define KDA_PIECE_CHUNKS 48
+#define KDA_PIECE_CHUNKS 80
 #endif
 namespace {
 constexpr long kSplitBelowHeads = 128;   // fewer heads than this: prep + state kernels
@@ -1396,8 +1396,9 @@ hipError_t launch_mfma_pieces(const void* q, const void* k, const void* v, const
     const long nch_seq = nch_all / B;
     char* rec = (char*)ws;
     float* carry = S_final ? S_final : (float*)(rec + (size_t)pairs * L * mf::REC_BYTES);
-    const size_t ws_piece = (size_t)pairs * L * mf::REC_BYTES;
-    const unsigned threads = ws_piece > (size_t(128) << 20) ? 832u : 768u;
+    // the records were just written and sit in the last-level cache: no
+    // L2-touch wave (it measured slower here)
+    const unsigned threads = 768u;
     const long groups = (pairs + 7) / 8;
     for (long c0 = 0; c0 < nch_seq; c0 += L) {
         const long Lc = std::min(L, nch_seq - c0);

@@ -206,7 +206,7 @@ def test_split_path_regimes_alternate_within_workgroup():
 def test_piecewise_split_path_all_heads():
     # Few heads with records that would outgrow the last-level cache: the
     # split path runs prep and state walk piece by piece along the sequence
-    # (B1 H4 T65536: eight pieces of 128 chunks), the state carried in S_final.
+    # (B1 H4 T65536: pieces of 160 chunks), the state carried in S_final.
     c = W.PREFILL_CONFIGS["long"]
     x = W.prefill_inputs(c, B=1, T=65536, H=4, seed=31)
     assert kda.kda_prefill_workspace_size(1, 65536, 4, 128, 128, torch.bfloat16) < 64 << 20
@@ -218,10 +218,11 @@ def test_piecewise_split_path_all_heads():
 @pytest.mark.parametrize("mode", ["S_final", "no_state", "in_place"])
 def test_piecewise_split_path_batch_ragged(mode):
     # Two sequences (strided windows of the batch), a carried S0 and a ragged
-    # last piece of one chunk of 33 tokens; the state carried in S_final, in
-    # the workspace (no S_final wanted), or in S0 itself (S_final = S0).
+    # last piece of one chunk of 33 tokens (801 chunks per sequence: five
+    # pieces of 160 and one); the state carried in S_final, in the workspace
+    # (no S_final wanted), or in S0 itself (S_final = S0).
     c = W.PREFILL_CONFIGS["batched"]
-    T = 49152 + 33
+    T = 800 * 64 + 33
     x = W.prefill_inputs(c, B=2, T=T, H=2, seed=32)
     xd = to_dev(x)
     if mode == "S_final":

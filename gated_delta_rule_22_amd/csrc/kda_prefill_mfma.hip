@@ -569,6 +569,8 @@ __device__ __forceinline__ void stage3(Prep& sm, const bf16* sV, int u0col, f32x
 
 // The three state passes for one chunk and this wave's 16 value columns:
 // U = U0 - W S, O = Q_decay S + M_qk U, S = Diag(a_last) S + K_restore^T U.
+// Every A operand comes from LDS in operand order (one 16-byte read per lane:
+// -W (I, kk), Q_decay (I, kk) at 4 I + kk, M_qk, K_restore^T (m, kk) at 2 m + kk).
 // O[I] receives rows 16I + 4g + (0..3) of column r (MFMA accumulator layout).
 // PRELOAD reads all LDS operands of a pass before its MFMAs so the reads
 // overlap (needs ~130 more registers); otherwise the reads run a few MFMA
@@ -579,8 +581,8 @@ struct NoOp { __device__ void operator()(int) const {} };
 
 template <bool PRELOAD, typename Between = NoOp>
 __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4],
-                                           const bf16x8 (*nW)[64], const bf16* Qdec,
-                                           const bf16x8 (*M)[64], const bf16* KrT,
+                                           const bf16x8 (*nW)[64], const bf16x8 (*Qop)[64],
+                                           const bf16x8 (*M)[64], const bf16x8 (*Krop)[64],
                                            const float* alast, f32x4 (&O)[4],
                                            Between between = Between())
 {
@@ -603,7 +605,7 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 aW[I][kk] = nW[I * 4 + kk][lane];
-                aQ[I][kk] = ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g);
+                aQ[I][kk] = Qop[I * 4 + kk][lane];
             }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -626,7 +628,7 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
         auto ld_wq = [&](int s, bf16x8& w, bf16x8& q) {
             const int I = s & 3, kk = s >> 2;
             w = nW[I * 4 + kk][lane];
-            q = ldA_perm(Qdec + (16 * I + r) * KS, 32 * kk, g);
+            q = Qop[I * 4 + kk][lane];
         };
 #pragma unroll
         for (int s = 0; s < D; ++s) ld_wq(s, bw[s], bq[s]);
@@ -653,8 +655,8 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
         bf16x8 bk[2][2];
         f32x4 bal[2];
         auto ld_k = [&](int m, bf16x8 (&kb)[2], f32x4& al) {
-            kb[0] = ldA_perm(KrT + (16 * m + r) * TS, 0, g);
-            kb[1] = ldA_perm(KrT + (16 * m + r) * TS, 32, g);
+            kb[0] = Krop[2 * m][lane];
+            kb[1] = Krop[2 * m + 1][lane];
             al = *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
         };
         ld_k(0, bk[0], bal[0]);
@@ -691,8 +693,8 @@ __device__ __forceinline__ void state_pass(f32x4 (&Sacc)[8], const f32x4 (&U0)[4
         f32x4 al[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            aK[m][0] = ldA_perm(KrT + (16 * m + r) * TS, 0, g);
-            aK[m][1] = ldA_perm(KrT + (16 * m + r) * TS, 32, g);
+            aK[m][0] = Krop[2 * m][lane];
+            aK[m][1] = Krop[2 * m + 1][lane];
             al[m] = *reinterpret_cast<const f32x4*>(&alast[16 * m + 4 * g]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -846,6 +848,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         f32x4 U0[4];
         stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
         lds_barrier();
+        // Q_decay and K_restore^T to A-operand order in the slots of K_decay
+        // and K_inv (dead since stage 2): each wave then reads every operand
+        // of the state pass with one conflict-free 16-byte load per lane,
+        // where reading the row-major tiles takes two 8-byte loads that
+        // collide in the LDS banks
+        bf16x8 (*Qop)[64] = reinterpret_cast<bf16x8 (*)[64]>(sm.Kd);
+        bf16x8 (*Krop)[64] = reinterpret_cast<bf16x8 (*)[64]>(sm.Ki);
+#pragma unroll
+        for (int e = wave; e < 32; e += NW) {
+            if (e < 16) {
+                Qop[e][lane] = ldA_perm(sm.Qd + (16 * (e >> 2) + r) * KS, 32 * (e & 3), g);
+            } else {
+                const int jj = e - 16;
+                Krop[jj][lane] = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g);
+            }
+        }
+        lds_barrier();
         // epilogue gate of this chunk in the output store's layout (lane t:
         // token t, this wave's 16 columns), fetched while the state pass runs
         uint4 zv[2];
@@ -857,7 +876,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
             zv[1] = *reinterpret_cast<const uint4*>(zp + 8);
         }
         f32x4 O[4];
-        state_pass<(NW < 8)>(Sacc, U0, sm.NWop, sm.Qd, sm.Mop, sm.KrT, sm.alast, O);
+        state_pass<(NW < 8)>(Sacc, U0, sm.NWop, Qop, sm.Mop, Krop, sm.alast, O);
         if constexpr (EPI) {
             __shared__ f32x4 epi_part[NW][C / 4];   // per wave: sum of o^2 over its 16 columns
             float s2[4][4];
@@ -888,8 +907,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
             store_o_gated(O, stf, zv, o, ((size_t)tok0 + (size_t)c * C) * H + h, (size_t)H,
                           16 * wave, ntok);
         } else {
-            // staging slots: waves 0-4 in Kd, 5-7 in Ki (both dead until the next chunk)
-            bf16* stage = (wave < 5) ? sm.Kd + wave * (C * OTS) : sm.Ki + (wave - 5) * (C * OTS);
+            // staging slots: waves 0-5 in RkT, 6-7 in sV (both dead since stage 3;
+            // other waves may still read Kd and Ki in their state pass)
+            bf16* stage = (wave < 6) ? sm.RkT + wave * (C * OTS) : sV + (wave - 6) * (C * OTS);
             store_o(O, stage, o, ((size_t)tok0 + (size_t)c * C) * H + h, (size_t)H, col0 + 16 * wave, ntok);
         }
         if (CKPT && ntok >= C && (c + 1) % ck_every == 0) {

@@ -845,25 +845,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         stage2<NW>(sm, fast);
         if (c + 1 < nchunks && !early_fetch) load_inputs<NW, DVB, PRO>(in, q, k, v, gate, beta, tok0, len, h, H, c + 1, col0);
         lds_barrier();
-        f32x4 U0[4];
-        stage3<NW, DVB>(sm, sV, 16 * wave, U0, fast);
-        lds_barrier();
         // Q_decay and K_restore^T to A-operand order in the slots of K_decay
-        // and K_inv (dead since stage 2): each wave then reads every operand
-        // of the state pass with one conflict-free 16-byte load per lane,
-        // where reading the row-major tiles takes two 8-byte loads that
-        // collide in the LDS banks
+        // and K_inv (dead since stage 2), one or two operands per wave after
+        // each block of the substitution, under its matrix work: each wave
+        // then reads every operand of the state pass with one conflict-free
+        // 16-byte load per lane, where reading the row-major tiles takes two
+        // 8-byte loads that collide in the LDS banks
         bf16x8 (*Qop)[64] = reinterpret_cast<bf16x8 (*)[64]>(sm.Kd);
         bf16x8 (*Krop)[64] = reinterpret_cast<bf16x8 (*)[64]>(sm.Ki);
+        auto to_operands = [&](int I) {
 #pragma unroll
-        for (int e = wave; e < 32; e += NW) {
-            if (e < 16) {
-                Qop[e][lane] = ldA_perm(sm.Qd + (16 * (e >> 2) + r) * KS, 32 * (e & 3), g);
-            } else {
-                const int jj = e - 16;
-                Krop[jj][lane] = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g);
+            for (int u = 0; u < 8 / NW; ++u) {
+                const int e = u * 4 * NW + I * NW + wave;   // 0 .. 31 over blocks and waves
+                if (e < 16) {
+                    Qop[e][lane] = ldA_perm(sm.Qd + (16 * (e >> 2) + r) * KS, 32 * (e & 3), g);
+                } else {
+                    const int jj = e - 16;
+                    Krop[jj][lane] = ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g);
+                }
             }
-        }
+        };
+        f32x4 U0[4];
+        stage3<NW, DVB, decltype(to_operands)>(sm, sV, 16 * wave, U0, fast, to_operands);
         lds_barrier();
         // epilogue gate of this chunk in the output store's layout (lane t:
         // token t, this wave's 16 columns), fetched while the state pass runs

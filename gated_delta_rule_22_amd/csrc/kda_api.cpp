@@ -64,7 +64,7 @@ const char* kda_status_string(kda_status s) {
 size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dtype,
                                   int chunk) {
     if (B <= 0 || T <= 0 || H <= 0 || dtype != KDA_BF16) return 0;
-    if (!kda::prefill_mfma_supported(dk, dv, chunk)) return 0;
+    if (!kda::prefill_mfma_supported(dk, dv, chunk, H)) return 0;
     return kda::prefill_mfma_workspace_fixed(B, H, ((long)T + kChunk - 1) / kChunk);
 }
 
@@ -119,7 +119,7 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     const kda::SeqLayout sq{nullptr, B, T, kChunk, 0, T};
-    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
+    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk, H)) {
         const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
         if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
         bool epi_done;
@@ -140,7 +140,7 @@ size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int 
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return 0;
     size_t need = varlen_table_bytes(N);
-    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk))
+    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk, H))
         need += kda::prefill_mfma_workspace((long)N * H, varlen_chunk_bound(N, T_total), H);
     return need;
 }
@@ -214,7 +214,7 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
     // With no tokens every sequence is empty and only S_final = S0 remains:
     // the generic kernel does that without touching a chunk record.
     bool epi_done;
-    if (dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk))
+    if (dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk, H))
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H,
                                      (int)varlen_chunk_bound(N, T_total),
                                      (char*)ws + varlen_table_bytes(N), S_ckpt, ckpt_slots, 0,
@@ -342,7 +342,7 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
     if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
     // the matrix-core path's log-decay range is [-5, 0]: a wider bounded
     // gate would be clamped there
-    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk) &&
+    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk, H) &&
         (cfg.pro & 3) == KDA_GATE_BOUNDED && cfg.pr.bound > 5.f)
         return KDA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return KDA_OK;
@@ -389,7 +389,7 @@ kda_status kda_prefill_layer(const void* q, const void* k, const void* v, const 
     const kda::SeqLayout sq{nullptr, B, T, kChunk, 0, T};
     hipError_t e;
     bool epi_done = false;
-    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk)) {
+    if (dtype == KDA_BF16 && T > 0 && kda::prefill_mfma_supported(dk, dv, chunk, H)) {
         const size_t nch = (size_t)B * (((size_t)T + kChunk - 1) / kChunk);
         if (nch > (size_t)INT32_MAX) return KDA_ERR_INVALID_ARG;
         const kda::Epilogue ep{cfg.z, cfg.w, cfg.out_eps};

@@ -59,7 +59,9 @@ hipError_t launch_prefill_generic(bool bf16_io, const void* q, const void* k, co
 // otherwise one fused kernel. With ep.z set, the 128-column fused kernel
 // applies the layer epilogue itself and *epi_done says so; otherwise the
 // caller runs launch_norm_gate afterwards.
-bool prefill_mfma_supported(int dk, int dv, int chunk);
+// Heads at most kMfmaMaxHeads (above: the generic path).
+constexpr long kMfmaMaxHeads = 65536;
+bool prefill_mfma_supported(int dk, int dv, int chunk, long H);
 bool prefill_mfma_split(long pairs);
 size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H);
 // Fixed-length batches (B sequences of nch_seq chunks): the workspace of the

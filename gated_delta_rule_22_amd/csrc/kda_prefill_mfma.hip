@@ -160,6 +160,11 @@ struct Inputs {
 // Loads are unconditional (tail tokens re-read the last token) and the raw
 // values are kept as loaded: tail tokens are zeroed where they are consumed,
 // so no instruction waits on a load before the next chunk is needed.
+// Buffer loads: the chunk's first row of head h is the (scalar) base of each
+// resource, a token's row a scalar offset and the lane's channels a vector
+// offset fixed for the whole call, so issuing a load costs no vector address
+// arithmetic. Offsets inside one chunk stay far below 2^31; each resource
+// ends after the chunk's last real row, so nothing past it is ever read.
 template <int NW, int DVB, int PRO, bool NT = false>
 __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restrict__ q,
                                             const bf16* __restrict__ k,
@@ -171,39 +176,65 @@ __device__ __forceinline__ void load_inputs(Inputs<NW>& in, const bf16* __restri
     constexpr int GM = PRO & 3;
     constexpr int TPT = C / NW;
     constexpr int VPR = DVB / 8;   // 16-byte pieces per value row
+    constexpr int AUX = NT ? 2 : 0;   // cache policy: non-temporal
+    constexpr int RSRC3 = 0x00020000;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int t0 = wave * TPT;
-    // token tok of the sequence starting at tok0 (len > 0 tokens)
-    auto row = [&](int tok) -> size_t { return ((size_t)tok0 + min(tok, len - 1)) * H + h; };
+    const int last = min(C, len - c * C) - 1;             // last real token of the chunk
+    const size_t row0 = ((size_t)tok0 + (size_t)c * C) * H + h;
+    const int rs2 = H * (DK * 2);                         // token stride of q, k (bytes)
+    const int n2 = last * rs2 + DK * 2;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + row0 * DK), 0, n2, RSRC3);
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + row0 * DK), 0, n2, RSRC3);
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
-        const size_t rw = row(c * C + t0 + j);
-        const size_t base = rw * DK + 2 * lane;
-        if constexpr (NT) {
-            in.k[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(k + base));
-            in.q[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q + base));
-        } else {
-            in.k[j] = *reinterpret_cast<const uint32_t*>(k + base);
-            in.q[j] = *reinterpret_cast<const uint32_t*>(q + base);
+        const int tok = min(t0 + j, last);
+        in.k[j] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane, tok * rs2, AUX);
+        in.q[j] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * lane, tok * rs2, AUX);
+    }
+    if constexpr (GM == kGateLog) {
+        const int rs4 = H * (DK * 4);
+        const auto rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const float*>(gate) + row0 * DK), 0, last * rs4 + DK * 4, RSRC3);
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rg, 8 * lane, min(t0 + j, last) * rs4, AUX);
+            in.la[j] = __builtin_bit_cast(f32x2, x);
         }
-        if constexpr (GM == kGateLog) {
-            const f32x2* lp = reinterpret_cast<const f32x2*>(static_cast<const float*>(gate) + base);
-            in.la[j] = NT ? __builtin_nontemporal_load(lp) : *lp;
-        } else if constexpr (GM == kGateBounded) {
-            const uint32_t bits = *reinterpret_cast<const uint32_t*>(static_cast<const bf16*>(gate) + base);
+    } else if constexpr (GM == kGateBounded) {
+        const auto rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const bf16*>(gate) + row0 * DK), 0, n2, RSRC3);
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rg, 4 * lane, min(t0 + j, last) * rs2, AUX);
             in.la[j] = f32x2{__builtin_bit_cast(float, bits), 0.f};
-        } else {
-            const float a = static_cast<const float*>(gate)[rw];
+        }
+    } else {
+        const auto rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const float*>(gate) + row0), 0, last * H * 4 + 4, RSRC3);
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const float a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rg, 0, min(t0 + j, last) * (H * 4), AUX));
             in.la[j] = f32x2{a, a};
         }
     }
+    const int rsv = H * 256;                              // token stride of v (bytes)
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + row0 * 128), 0, last * rsv + 256, RSRC3);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int piece = tid + p * NW * 64;
         const int t = piece / VPR, c8 = piece - t * VPR;
-        in.v[p] = *reinterpret_cast<const uint4*>(v + row(c * C + t) * 128 + col0 + 8 * c8);
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+            rv, min(t, last) * rsv + (col0 + 8 * c8) * 2, 0, AUX);
+        in.v[p] = make_uint4(x[0], x[1], x[2], x[3]);
     }
-    if (tid < C) in.beta = beta[row(c * C + tid)];
+    if (tid < C) {
+        const auto rb = __builtin_amdgcn_make_buffer_rsrc((void*)(beta + row0), 0, last * H * 4 + 4, RSRC3);
+        in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, min(tid, last) * (H * 4), 0, AUX));
+    }
 }
 
 // Layer prologue on a chunk's inputs, before stage 1a: the bounded gate's
@@ -1358,8 +1389,9 @@ constexpr size_t kPieceAbove = size_t(192) << 20;
 constexpr long kPieceMinWork = 512;      // chunk-heads per piece, at least
 }
 
-bool prefill_mfma_supported(int dk, int dv, int chunk) {
-    return dk == 128 && dv == 128 && (chunk == 64 || chunk == 0);
+bool prefill_mfma_supported(int dk, int dv, int chunk, long H) {
+    // H: the chunk loads address one chunk of all heads with 32-bit offsets
+    return dk == 128 && dv == 128 && (chunk == 64 || chunk == 0) && H <= kMfmaMaxHeads;
 }
 
 bool prefill_mfma_split(long pairs) { return pairs < kSplitBelowHeads; }

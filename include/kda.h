@@ -39,7 +39,9 @@
  * [-5, 0], kda_decode_multi drafts of 2..8 tokens into [-10, 0]. A step that
  * decays harder than the floor keeps exp(floor) of the old state (0.7% for
  * the prefill) instead of less; its error is that fraction of the old
- * state's contribution.
+ * state's contribution. The bf16 matrix-core prefill runs for up to 65536
+ * heads; calls with more take the generic bf16 kernels (same results up to
+ * rounding, slower).
  */
 #ifndef KDA_H
 #define KDA_H

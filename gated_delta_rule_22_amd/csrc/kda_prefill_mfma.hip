@@ -1005,8 +1005,10 @@ struct ChunkMap {
 
 // Prep kernel: chunks [gc0, gc0 + cpw) of the chunk numbering, head h;
 // writes the operand record of chunk gc at record h * nch_all + gc. kTable:
-// the sequences come from a device table (fewer than 128 of them).
-template <bool kTable, int PRO>
+// the sequences come from a device table (fewer than 128 of them). NT: the
+// inputs are read non-temporally, so that streaming a long sequence through
+// leaves the last-level cache to the records.
+template <bool kTable, int PRO, bool NT>
 __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const void* __restrict__ gate, const float* __restrict__ beta,
@@ -1028,7 +1030,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     ChunkPos p{0, 1, 0};
     if (gc0 < gc1) {
         p = map.at(gc0);
-        load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, p.tok0, p.len, h, H, p.c, 0);
+        load_inputs<NW, DVB, PRO, NT>(in, q, k, v, gate, beta, p.tok0, p.len, h, H, p.c, 0);
     }
     for (int gc = gc0; gc < gc1; ++gc) {
         const int ntok = p.len - p.c * C;
@@ -1048,7 +1050,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
         }
         // next chunk's inputs: waves 0-3 now; waves 4-7 (lighter Gram work)
         // after stage 2, so their fetches queue while the inverses finish
-        if (more && wave < 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        if (more && wave < 4) load_inputs<NW, DVB, PRO, NT>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         char* rec = ws + ((size_t)h * nch_all + gc) * REC_BYTES;
         const int g = lane >> 4, r = lane & 15;
@@ -1076,7 +1078,7 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
                     ldA_perm(sm.KrT + (16 * (jj >> 1) + r) * TS, 32 * (jj & 1), g);
             }
         }
-        if (more && wave >= 4) load_inputs<NW, DVB, PRO, true>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
+        if (more && wave >= 4) load_inputs<NW, DVB, PRO, NT>(in, q, k, v, gate, beta, pn.tok0, pn.len, h, H, pn.c, 0);
         lds_barrier();
         // Operand record stores (16 B per lane per A operand), each placed
         // where it overlaps other work:
@@ -1474,7 +1476,7 @@ hipError_t launch_mfma_pieces(const void* q, const void* k, const void* v, const
         int cpw = (int)((work + 255) / 256);
         if (cpw < 1) cpw = 1;
         const long ngrp = (nch_piece + cpw - 1) / cpw;
-        hipLaunchKernelGGL((prefill_prep_kernel<false, PRO>), dim3((unsigned)(H * ngrp)), dim3(512),
+        hipLaunchKernelGGL((prefill_prep_kernel<false, PRO, true>), dim3((unsigned)(H * ngrp)), dim3(512),
                            0, st, qp, kp, vp, gp, bp, rec, sp, H, cpw, nch_piece, pr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1520,9 +1522,11 @@ hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const vo
         if (cpw < 1) cpw = 1;
         const long ngrp = (nch_all + cpw - 1) / cpw;
         // (the layer forms take fixed-length batches only: no table variant)
-        auto prep = prefill_prep_kernel<false, PRO>;
+        // (cached input loads: with the records of the whole call under the
+        // piecewise threshold they measure faster here than non-temporal ones)
+        auto prep = prefill_prep_kernel<false, PRO, false>;
         if constexpr (PRO == 0)
-            if (sq.tab) prep = prefill_prep_kernel<true, 0>;
+            if (sq.tab) prep = prefill_prep_kernel<true, 0, false>;
         hipLaunchKernelGGL(prep, dim3((unsigned)(H * ngrp)), dim3(512), 0, st, (const bf16*)q,
                            (const bf16*)k, (const bf16*)v, gate, beta, (char*)ws, sq, H, cpw,
                            nch_all, pr);

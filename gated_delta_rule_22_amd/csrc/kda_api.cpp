@@ -140,8 +140,11 @@ size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int 
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return 0;
     size_t need = varlen_table_bytes(N);
-    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk, H))
+    if (dtype == KDA_BF16 && kda::prefill_mfma_supported(dk, dv, chunk, H)) {
         need += kda::prefill_mfma_workspace((long)N * H, varlen_chunk_bound(N, T_total), H);
+        const kda::SplitPlan plan = kda::prefill_split_plan(N, T_total, H, need);
+        if (plan.n2 > 0) need = plan.end;
+    }
     return need;
 }
 
@@ -214,7 +217,16 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
     // With no tokens every sequence is empty and only S_final = S0 remains:
     // the generic kernel does that without touching a chunk record.
     bool epi_done;
-    if (dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk, H))
+    const bool mfma = dtype == KDA_BF16 && T_total > 0 && kda::prefill_mfma_supported(dk, dv, chunk, H);
+    const kda::SplitPlan plan =
+        mfma ? kda::prefill_split_plan(N, T_total, H, varlen_table_bytes(N)) : kda::SplitPlan{};
+    if (plan.n2 > 0)
+        // many sequence-heads, lengths decided on the device: sequences far
+        // longer than the rest are split between the fused kernel and the
+        // prep + state walk
+        e = kda::launch_prefill_split(q, k, v, log_alpha, beta, S0, o, S_final, tab, N, T_total,
+                                      ckpt_every, H, plan, (char*)ws, S_ckpt, ckpt_slots, st);
+    else if (mfma)
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H,
                                      (int)varlen_chunk_bound(N, T_total),
                                      (char*)ws + varlen_table_bytes(N), S_ckpt, ckpt_slots, 0,

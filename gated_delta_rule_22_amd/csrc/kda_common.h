@@ -80,6 +80,18 @@ __device__ __forceinline__ int wave_id() {
 // sequence i has len(i) / K checkpoints, the states after K, 2K, ... tokens.
 // Without a table, sequence i starts at token i * S (S >= T: a window of T
 // tokens of longer sequences, as the piecewise prefill walks them).
+//
+// Split schedule of a packed call (all null otherwise; see varlen_split in
+// kda_varlen.hip): a long sequence runs its first segment in the fused
+// kernel and the rest as an entry of a second table that the prep and state
+// kernels walk.
+//   lens  explicit entry lengths: entry i covers [tab[i], tab[i] + lens[i])
+//         (the entries need not tile the token axis)
+//   ord   fused kernel: sequence of the j-th group of workgroups (longest first)
+//   mslot fused kernel: slot of sequence i's first-segment end state in mid,
+//         -1 when it is not split
+//   fin   state kernel: original sequence of entry i (its S_final row), -1 for
+//         an unused entry (its workgroups exit at once)
 struct SeqLayout {
     const int* tab;
     int N;   // sequences
@@ -87,8 +99,15 @@ struct SeqLayout {
     int C;   // chunk length of the chunk numbering
     int K;   // checkpoint interval, 0 = none
     long S;  // tokens between sequence starts (no table)
+    const int* lens = nullptr;
+    const int* ord = nullptr;
+    const int* mslot = nullptr;
+    const int* fin = nullptr;
+    float* mid = nullptr;
     __device__ long start(int i) const { return tab ? (long)tab[i] : (long)i * S; }
-    __device__ int len(int i) const { return tab ? tab[i + 1] - tab[i] : T; }
+    __device__ int len(int i) const {
+        return lens ? lens[i] : (tab ? tab[i + 1] - tab[i] : T);
+    }
     __device__ long chunk0(int i) const {
         return tab ? (long)tab[N + 1 + i] : (long)i * ((T + C - 1) / C);
     }

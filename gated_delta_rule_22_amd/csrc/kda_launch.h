@@ -37,6 +37,12 @@ hipError_t launch_decode_multi(bool bf16_io, int dk, int dv, const void* q, cons
 hipError_t launch_varlen_table(const int* cu, int N, int T, int C, int K, int* tab,
                                hipStream_t st);
 
+// Split schedule of a packed call (kda_varlen.hip): from the table of
+// launch_varlen_table, the fused view of every sequence and a second table
+// of the long sequences' second segments, into `out` (SplitPlan::sp).
+hipError_t launch_varlen_split(const int* tab, int N, int T, int C, int K, int H, int n2,
+                               int cap2, int* out, hipStream_t st);
+
 // Multi-token decode on the matrix cores (bf16, dk = dv = 128, 2 <= ntok <= 8).
 bool decode_multi_mfma_supported(bool bf16_io, int dk, int dv, int ntok);
 hipError_t launch_decode_multi_mfma(const void* q, const void* k, const void* v, const float* la,
@@ -75,6 +81,27 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                const SeqLayout& sq, int H, int nch_all, void* ws,
                                float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
                                const Epilogue& ep, bool* epi_done, hipStream_t st);
+
+// Split schedule of a packed call with many sequence-heads (N * H >= 256,
+// N <= 1024): workspace layout after the sequence table (at byte `base`):
+//   sp   ints: ord, lens1, mslot [N]; tab2 [3 n2 + 3]; lens2, fin2 [n2]
+//   mid  first-segment end states, [n2][H][128][128] fp32
+//   rec  operand records of the second segments, H * cap2 of them
+// n2 == 0: the schedule does not apply (plain fused kernel).
+struct SplitPlan {
+    int n2 = 0;       // second-table entries, at most
+    int cap2 = 0;     // second-segment chunks in all, at most
+    int G = 0;        // prep workgroups per head
+    size_t sp = 0, mid = 0, rec = 0, end = 0;
+};
+SplitPlan prefill_split_plan(int N, int T_total, int H, size_t base);
+// Runs the schedule: the mixed fused + prep kernel, then the state walk of
+// the second segments. tab = the sequence table, sp = SplitPlan::sp.
+hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* la,
+                                const float* beta, const float* S0, void* o, float* S_final,
+                                const int* tab, int N, int T_total, int K, int H,
+                                const SplitPlan& plan, char* ws, float* S_ckpt, int ck_slots,
+                                hipStream_t st);
 
 // Layer epilogue over rows of dv values (one token and head each), in place
 // allowed: out = w * o / sqrt(mean(o^2) + eps) * sigmoid(z); w may be null.

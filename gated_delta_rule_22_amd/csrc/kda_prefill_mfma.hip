@@ -515,10 +515,18 @@ __device__ __forceinline__ void stage2(Prep& sm, bool fast) {
 #pragma unroll
                 for (int j = 0; j < i; ++j) p[j] -= y[i] * row[i % 3][j / 4][j % 4];
             }
+            // lane (g, r) keeps y[4g .. 4g + 3], picked with bit masks:
+            // conditionals here compile to divergent branches or to an
+            // indexed copy of y in scratch memory
             f32x4 d;
+            const uint32_t m1 = (g & 1) ? ~0u : 0u, m2 = (g & 2) ? ~0u : 0u;
+            auto pick = [](uint32_t m, float a, float b) {   // m ? b : a
+                return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, a) & ~m) |
+                                                     (__builtin_bit_cast(uint32_t, b) & m));
+            };
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                d[i] = (g == 0) ? y[i] : (g == 1) ? y[4 + i] : (g == 2) ? y[8 + i] : y[12 + i];
+                d[i] = pick(m2, pick(m1, y[i], y[4 + i]), pick(m1, y[8 + i], y[12 + i]));
             sm.Dt[I][lane] = __builtin_convertvector(d, bf16x4);
         }
     }
@@ -812,24 +820,29 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&Sacc)[8], 
 // row's columns is reduced inside each wave's 16 columns by DPP and across
 // the eight waves through LDS, and z, fetched at the chunk start in the
 // accumulator layout, gates the result.
+// The body takes the LDS blocks and its block index from the kernel that
+// runs it (the fused kernel, or the split schedule's mixed kernel). With
+// sq.ord the j-th group of H workgroups takes sequence sq.ord[j]; with
+// sq.mslot a split sequence leaves its end state in sq.mid instead of S_final.
 template <int NW, bool CKPT, int PRO, bool EPI = false>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
+__device__ __forceinline__ void fused_body(
+    mf::Prep& sm, bf16* sV, int blk,
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const void* __restrict__ gate, const float* __restrict__ beta,
-    const float* S0, bf16* __restrict__ o, float* S_final, SeqLayout sq, int H, int NVB,
-    float* __restrict__ S_ckpt, int ck_slots, Prologue pr, Epilogue ep)
+    const float* S0, bf16* __restrict__ o, float* S_final, const SeqLayout& sq, int H, int NVB,
+    float* __restrict__ S_ckpt, int ck_slots, const Prologue& pr, const Epilogue& ep)
 {
     static_assert(!EPI || NW == 8, "the fused epilogue needs the whole row in one workgroup");
     using namespace mf;
     constexpr int DVB = NW * 16;
-    __shared__ Prep sm;
-    __shared__ __attribute__((aligned(16))) bf16 sV[C * (DVB + 8)];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
-    const int vb = blockIdx.x % NVB;
-    const int bh = blockIdx.x / NVB;
-    const int b = bh / H, h = bh - b * H;
+    const int vb = blk % NVB;
+    const int bh0 = blk / NVB;
+    const int j = bh0 / H, h = bh0 - j * H;
+    const int b = sq.ord ? sq.ord[j] : j;
+    const int bh = b * H + h;
     const int col0 = vb * DVB;
     const int ncol = col0 + 16 * wave + r;
     const long tok0 = sq.start(b);
@@ -952,7 +965,22 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
         }
     }
 
-    if (S_final) store_state(S_final + sbase, Sacc, g, ncol);
+    const int ms = sq.mslot ? sq.mslot[b] : -1;
+    if (ms >= 0) store_state(sq.mid + ((size_t)ms * H + h) * DK * 128, Sacc, g, ncol);
+    else if (S_final) store_state(S_final + sbase, Sacc, g, ncol);
+}
+
+template <int NW, bool CKPT, int PRO, bool EPI = false>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_fused_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const void* __restrict__ gate, const float* __restrict__ beta,
+    const float* S0, bf16* __restrict__ o, float* S_final, SeqLayout sq, int H, int NVB,
+    float* __restrict__ S_ckpt, int ck_slots, Prologue pr, Epilogue ep)
+{
+    __shared__ mf::Prep sm;
+    __shared__ __attribute__((aligned(16))) bf16 sV[mf::C * (NW * 16 + 8)];
+    fused_body<NW, CKPT, PRO, EPI>(sm, sV, blockIdx.x, q, k, v, gate, beta, S0, o, S_final, sq, H,
+                                   NVB, S_ckpt, ck_slots, pr, ep);
 }
 
 // Chunk numbering of the prep kernel, for fewer than 128 sequences: chunk gc
@@ -966,6 +994,7 @@ struct ChunkMap {
     SeqLayout sq;
     int nch;              // without a table: chunks per sequence
     int off[2], cst[2];   // with a table: offset and first chunk of entries lane, 64 + lane
+    int ln[2];            // with explicit lengths (sq.lens): their lengths
     __device__ explicit ChunkMap(const SeqLayout& s) : sq(s), nch((s.T + mf::C - 1) / mf::C) {
         if (kTable) {
             const int lane = threadIdx.x & 63;
@@ -974,6 +1003,7 @@ struct ChunkMap {
                 const int j = min(lane + 64 * u, s.N);   // entries past N repeat entry N
                 off[u] = s.tab[j];
                 cst[u] = (lane + 64 * u <= s.N) ? s.tab[s.N + 1 + j] : 0x7fffffff;
+                ln[u] = s.lens ? s.lens[min(j, s.N - 1)] : 0;
             }
         }
     }
@@ -991,7 +1021,8 @@ struct ChunkMap {
         const int i = __builtin_popcountll(__builtin_amdgcn_ballot_w64(cst[0] <= gc)) +
                       __builtin_popcountll(__builtin_amdgcn_ballot_w64(cst[1] <= gc)) - 1;
         const int o0 = entry(off, i);
-        return {(long)o0, entry(off, i + 1) - o0, gc - entry(cst, i)};
+        const int len = sq.lens ? entry(ln, i) : entry(off, i + 1) - o0;
+        return {(long)o0, len, gc - entry(cst, i)};
     }
     // position of chunk gc + 1 given that of chunk gc
     __device__ ChunkPos next(const ChunkPos& p, int gc) const {
@@ -1008,21 +1039,19 @@ struct ChunkMap {
 // the sequences come from a device table (fewer than 128 of them). NT: the
 // inputs are read non-temporally, so that streaming a long sequence through
 // leaves the last-level cache to the records.
+// The body runs chunks [gc0, gc0 + cpw) of head h (clamped to the
+// numbering's end); the kernel that runs it passes the LDS blocks.
 template <bool kTable, int PRO, bool NT>
-__global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
+__device__ __forceinline__ void prep_body(
+    mf::Prep& sm, bf16* sV, int h, int gc0, int cpw,
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const void* __restrict__ gate, const float* __restrict__ beta,
-    char* __restrict__ ws, SeqLayout sq, int H, int cpw, int nch_all, Prologue pr)
+    char* __restrict__ ws, const SeqLayout& sq, int H, int nch_all, const Prologue& pr)
 {
     using namespace mf;
     constexpr int NW = 8, DVB = 128;
-    __shared__ Prep sm;
-    __shared__ __attribute__((aligned(16))) bf16 sV[C * (DVB + 8)];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int ngrp = (nch_all + cpw - 1) / cpw;
-    const int h = blockIdx.x / ngrp;
-    const int gc0 = (blockIdx.x - h * ngrp) * cpw;
     const ChunkMap<kTable> map(sq);
     const int gc1 = min(gc0 + cpw, map.total());
 
@@ -1115,6 +1144,20 @@ __global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
     }
 }
 
+template <bool kTable, int PRO, bool NT>
+__global__ __launch_bounds__(512, 1) void prefill_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const void* __restrict__ gate, const float* __restrict__ beta,
+    char* __restrict__ ws, SeqLayout sq, int H, int cpw, int nch_all, Prologue pr)
+{
+    __shared__ mf::Prep sm;
+    __shared__ __attribute__((aligned(16))) bf16 sV[mf::C * (128 + 8)];
+    const int ngrp = (nch_all + cpw - 1) / cpw;
+    const int h = blockIdx.x / ngrp;
+    const int gc0 = (blockIdx.x - h * ngrp) * cpw;
+    prep_body<kTable, PRO, NT>(sm, sV, h, gc0, cpw, q, k, v, gate, beta, ws, sq, H, nch_all, pr);
+}
+
 // State kernel: one workgroup of twelve waves per (sequence*head, 16 value
 // columns). Each wave has one role, so the chunk-to-chunk chain is two short
 // MFMA passes and every wave loads only the few operands it uses:
@@ -1157,11 +1200,14 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
     const int ct = (blockIdx.x >> 3) & 7;          // value column tile
     if (bh >= BH) return;                          // whole workgroup: uniform
     const int b = bh / H, h = bh - b * H;          // sequence b, head h
+    if (sq.fin && sq.fin[b] < 0) return;           // unused entry of a split schedule
     const int ncol = 16 * ct + r;
     const long tok0 = sq.start(b);
     const int T = sq.len(b);
     const int nchunks = (T + C - 1) / C;
     const size_t sbase = (size_t)bh * DK * 128;
+    // S_final row: the entry's own, or that of the sequence it continues
+    const size_t fbase = sq.fin ? ((size_t)sq.fin[b] * H + h) * DK * 128 : sbase;
     // An empty sequence walks no chunk: its waves fetch record 0 of the
     // workspace (unused) and the S waves store S_final = S0.
     const size_t rbase = nchunks > 0 ? (size_t)h * nch_all + sq.chunk0(b) : 0;
@@ -1280,7 +1326,7 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S_final[sbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+                    S_final[fbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol] = Sacc[m][i];
         }
     } else if (wave == 12) {
         // ---- L2 prefetch (launched only for workspaces that stream from HBM):
@@ -1371,6 +1417,35 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
         if (I < 2) run(std::true_type{});
         else run(std::false_type{});
     }
+}
+
+// Split schedule of a packed call, first launch: workgroups [0, nfused) run
+// the fused kernel on every sequence (sq1: longest first, split sequences on
+// their first segment, whose end state goes to sq1.mid); the other G per
+// head prepare the records of the second segments (table sq2), each a
+// consecutive share of that head's second-segment chunks. Both halves hold
+// the same LDS blocks, so the grid mixes them freely.
+template <bool CKPT>
+__global__ __launch_bounds__(512, 1) void prefill_split_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ la, const float* __restrict__ beta, const float* S0,
+    bf16* __restrict__ o, float* S_final, SeqLayout sq1, SeqLayout sq2, int H, int nfused,
+    int G, char* __restrict__ ws, int nrec, float* __restrict__ S_ckpt, int ck_slots)
+{
+    __shared__ mf::Prep sm;
+    __shared__ __attribute__((aligned(16))) bf16 sV[mf::C * (128 + 8)];
+    const int blk = blockIdx.x;
+    if (blk < nfused) {
+        fused_body<8, CKPT, 0>(sm, sV, blk, q, k, v, la, beta, S0, o, S_final, sq1, H, 1, S_ckpt,
+                               ck_slots, Prologue{}, Epilogue{});
+        return;
+    }
+    const int p = blk - nfused, h = p / G, grp = p - h * G;
+    const int total2 = sq2.tab[2 * sq2.N + 1];
+    const int cpw = (total2 + G - 1) / G;
+    if (grp * cpw >= total2) return;                 // whole workgroup: uniform
+    prep_body<true, 0, false>(sm, sV, h, grp * cpw, cpw, q, k, v, la, beta, ws, sq2, H, nrec,
+                              Prologue{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1545,6 +1620,68 @@ hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const vo
 }
 
 }  // namespace
+
+SplitPlan prefill_split_plan(int N, int T_total, int H, size_t base) {
+    SplitPlan p;
+    // the fused part runs one 8-wave workgroup per (sequence, head); the
+    // split table is built by one workgroup of 1024 threads
+    if ((long)N * H < 256 || N > 1024 || T_total <= 0) return p;
+    // a split sequence has more than total * H / 256 chunks, so fewer than
+    // 256 / H of them exist; the prep's chunk map holds up to 127 entries
+    p.n2 = std::min(std::min(N, 127), (256 + H - 1) / H);
+    const long nb = ((long)T_total + (long)N * (mf::C - 1)) / mf::C;   // chunks, at most
+    // records of at most 16384 chunk-heads (1.18 GB)
+    p.cap2 = (int)std::min(nb, std::max(64L, 16384L / H));
+    p.G = std::max(1, 512 / H);
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    p.sp = al(base);
+    p.mid = al(p.sp + (3 * (size_t)N + 5 * (size_t)p.n2 + 3) * sizeof(int));
+    p.rec = al(p.mid + (size_t)p.n2 * H * DK_STATE_BYTES);
+    p.end = p.rec + (size_t)H * p.cap2 * mf::REC_BYTES;
+    return p;
+}
+
+hipError_t launch_prefill_split(const void* q, const void* k, const void* v, const float* la,
+                                const float* beta, const float* S0, void* o, float* S_final,
+                                const int* tab, int N, int T_total, int K, int H,
+                                const SplitPlan& plan, char* ws, float* S_ckpt, int ck_slots,
+                                hipStream_t st)
+{
+    const int n2 = plan.n2;
+    int* sp = reinterpret_cast<int*>(ws + plan.sp);
+    hipError_t e = launch_varlen_split(tab, N, T_total, mf::C, K, H, n2, plan.cap2, sp, st);
+    if (e != hipSuccess) return e;
+    float* mid = reinterpret_cast<float*>(ws + plan.mid);
+    char* rec = ws + plan.rec;
+    SeqLayout sq1{tab, N, T_total, mf::C, K, T_total};
+    sq1.lens = sp + N;
+    sq1.ord = sp;
+    sq1.mslot = sp + 2 * N;
+    sq1.mid = mid;
+    const int* tab2 = sp + 3 * N;
+    SeqLayout sq2{tab2, n2, T_total, mf::C, K, T_total};
+    sq2.lens = tab2 + 3 * n2 + 3;
+    sq2.fin = sq2.lens + n2;
+    const bool ck = S_ckpt != nullptr && K > 0 && ck_slots > 0;
+    const int nfused = N * H;
+    const long grid = (long)nfused + (long)H * plan.G;
+    hipLaunchKernelGGL(ck ? prefill_split_kernel<true> : prefill_split_kernel<false>,
+                       dim3((unsigned)grid), dim3(512), 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, la, beta, S0, (bf16*)o, S_final, sq1, sq2, H, nfused,
+                       plan.G, rec, plan.cap2, S_ckpt, ck_slots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long BH2 = (long)n2 * H;
+    const long groups = (BH2 + 7) / 8;
+    // records that may outgrow half the last-level cache: L2-touch wave
+    const size_t rec_bytes = (size_t)H * plan.cap2 * mf::REC_BYTES;
+    const unsigned threads = rec_bytes > (size_t(128) << 20) ? 832u : 768u;
+    hipLaunchKernelGGL(ck ? prefill_state_kernel<true> : prefill_state_kernel<false>,
+                       dim3((unsigned)(groups * 64)), dim3(threads), 0, st, (const char*)rec,
+                       (const float*)mid, (bf16*)o, S_final, sq2, H, (int)BH2, plan.cap2, S_ckpt,
+                       ck_slots);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* gate,
                                const float* beta, const float* S0, void* o, float* S_final,

@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kTabThreads = 1024;
 constexpr int kTabWaves = kTabThreads / kWave;
+constexpr int kSplitCUs = 256;   // compute units of the GPU (MI355X)
 
 // Inclusive scan (running max, or running sum) of one value per thread over
 // the workgroup; `total` receives the workgroup-wide result. `sh` holds one
@@ -83,7 +84,114 @@ __global__ __launch_bounds__(kTabThreads) void varlen_table_kernel(
     }
 }
 
+// Split schedule of a packed call (the many-head fused path): a sequence
+// whose chunk count exceeds what one compute unit would get with the work
+// spread evenly (M = ceil(total chunks * H / 256)) would alone set the
+// call's length, since the fused kernel walks each (sequence, head) in one
+// workgroup. Such a sequence keeps its first m chunks in the fused kernel
+// (m = M rounded down to whole checkpoint intervals) and hands the rest to
+// the chunk-parallel prep and the state walk, as an entry of a second table.
+// Candidates (at least 8 chunks beyond m) are taken in index order while at
+// most n2 of them and at most cap2 second-segment chunks in all are taken;
+// the candidate that reaches cap2 is cut shorter (its first segment grows).
+// Fused workgroups take the sequences longest first (by first-segment
+// length), so the longest chains start at once. Output (ints, layout of
+// SplitTables in kda_launch.h): ord, lens1, mslot [N]; tab2 [3 n2 + 3];
+// lens2, fin2 [n2].
+__global__ __launch_bounds__(kTabThreads) void varlen_split_kernel(
+    const int* __restrict__ tab, int N, int T, int C, int K, int H, int n2, int cap2,
+    int* __restrict__ out)
+{
+    __shared__ int sh[2][kTabWaves];
+    __shared__ int key[kTabThreads];
+    const int i = threadIdx.x;
+    const bool live = i < N;
+    const int total = tab[2 * N + 1];
+    const int M = (int)(((long long)total * H + kSplitCUs - 1) / kSplitCUs);
+    const int kc = K > 0 ? K / C : 1;                       // chunks per checkpoint interval
+    const int mA = max(kc, (M / kc) * kc);
+    const int st = live ? tab[i] : 0;
+    const int len = live ? tab[i + 1] - st : 0;
+    const int nch = len / C + (len % C != 0);
+    const bool cand = live && nch >= mA + 8;
+    const int want = cand ? nch - mA : 0;
+    int tw, tc;
+    const int pw = block_scan<false>(want, sh[0], tw);       // inclusive
+    const int pc = block_scan<false>(cand ? 1 : 0, sh[1], tc);
+    const int before = pw - want;                            // second-segment chunks taken before i
+    int m = nch;                                             // first-segment chunks
+    bool taken = cand && pc <= n2 && before < cap2;
+    if (taken) {
+        const int n2c = min(want, cap2 - before);
+        m = ((nch - n2c + kc - 1) / kc) * kc;
+        if (nch - m < 8) {
+            taken = false;
+            m = nch;
+        }
+    }
+    const int len1 = taken ? m * C : len;
+    int* ord = out;
+    int* lens1 = out + N;
+    int* mslot = out + 2 * N;
+    int* tab2 = out + 3 * N;
+    int* lens2 = tab2 + 3 * n2 + 3;
+    int* fin2 = lens2 + n2;
+    // taken candidates form a prefix of the candidates: entry j = pc - 1
+    if (live) {
+        lens1[i] = len1;
+        mslot[i] = taken ? pc - 1 : -1;
+    }
+    if (taken) {
+        const int j = pc - 1;
+        tab2[j] = st + m * C;
+        tab2[n2 + 1 + j] = before;
+        tab2[2 * n2 + 2 + j] = K > 0 ? tab[2 * N + 2 + i] + m * C / K : 0;
+        lens2[j] = len - m * C;
+        fin2[j] = i;
+    }
+    // second-segment chunks actually taken: those of the last taken entry end it
+    key[i] = taken ? before + (nch - m) : 0;
+    __syncthreads();
+    int total2 = 0, nl = 0;
+    for (int u = 0; u < N; ++u) {
+        total2 = max(total2, key[u]);
+        nl += key[u] > 0;
+    }
+    for (int j = nl + i; j < n2; j += kTabThreads) {         // unused entries
+        tab2[j] = T;
+        tab2[n2 + 1 + j] = total2;
+        tab2[2 * n2 + 2 + j] = 0;
+        lens2[j] = 0;
+        fin2[j] = -1;
+    }
+    if (i == 0) {
+        tab2[n2] = T;
+        tab2[2 * n2 + 1] = total2;
+        tab2[3 * n2 + 2] = 0;
+    }
+    __syncthreads();
+    // longest first: rank by first-segment length, ties by index
+    key[i] = live ? len1 : -1;
+    __syncthreads();
+    if (live) {
+        int rank = 0;
+        for (int u = 0; u < N; ++u) {
+            const int ku = key[u];
+            rank += (ku > len1) || (ku == len1 && u < i);
+        }
+        ord[rank] = i;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_varlen_split(const int* tab, int N, int T, int C, int K, int H, int n2,
+                               int cap2, int* out, hipStream_t st) {
+    if (N > kTabThreads) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(varlen_split_kernel, dim3(1), dim3(kTabThreads), 0, st, tab, N, T, C, K, H,
+                       n2, cap2, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_varlen_table(const int* cu, int N, int T, int C, int K, int* tab,
                                hipStream_t st) {

@@ -171,6 +171,14 @@ def test_varlen_workspace_query(lib):
     assert few > tab and (few - tab) % (2 * ((300 + 3 * 63) // 64)) == 0
     assert f(0, 300, 2, 128, 128, 1, 64) == 0
     assert f(3, 300, 2, 48, 128, 1, 64) == 0         # unsupported
+    # 576 sequence-heads: the split schedule's tables, end states and records
+    # (at most 16384 chunk-heads of 72,192 B)
+    rec = 16384 * 72192
+    big = f(18, 65536, 32, 128, 128, 1, 64)
+    assert rec < big < rec + (64 << 20)
+    assert f(18, 65536, 32, 128, 128, 0, 64) == 256  # fp32: no split schedule
+    # more than 1024 sequences: table only
+    assert f(1025, 65536, 32, 128, 128, 1, 64) == (3 * 1025 + 3) * 4 + 255 & ~255
 
 
 @no_gpu

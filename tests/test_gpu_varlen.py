@@ -73,6 +73,78 @@ def test_bf16_paths(lengths, H, ckpt):
           run_oracle(x, ckpt), TOL_BF16)
 
 
+# The split schedule (N * H >= 256): a sequence longer than its share of an
+# evenly spread call, M = ceil(total chunks * H / 256) chunks, runs its first
+# m chunks in the fused kernel (m = M rounded down to whole checkpoint
+# intervals) and the rest in the prep + state walk, from the fused part's
+# end state. split_slots() reads back which sequences the device split.
+def split_slots(ws, N):
+    """mslot of the split schedule's tables in a varlen workspace: the tables
+    follow the 256-aligned sequence table of 3N + 3 ints as ord, lens1, mslot
+    [N] (the library's workspace layout for this schedule)."""
+    sp = ((3 * N + 3) * 4 + 255) & ~255
+    ints = ws[sp:sp + 12 * N].cpu().view(torch.int32)
+    return ints[2 * N:3 * N].tolist()
+
+
+@pytest.mark.parametrize("lengths,H,ckpt,split", [
+    ([64, 2048, 64, 64, 1, 64, 64, 64], 32, 0, [1]),              # m = 5 chunks
+    ([64, 2048, 64, 64, 1, 64, 64, 64], 32, 512, [1]),            # m = 8: one checkpoint each side
+    ([3000, 100, 0, 65, 2500] + [64] * 11, 16, 128, [0, 4]),      # two split, ragged ends
+])
+def test_bf16_split_schedule(lengths, H, ckpt, split):
+    x = W.varlen_inputs(BASE, lengths, H=H, seed=31)
+    N, T = len(lengths), sum(lengths)
+    nbytes = kda.kda_prefill_varlen_workspace_size(N, T, H, 128, 128, torch.bfloat16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    got = run_gpu(x, ckpt_every=ckpt, workspace=ws)
+    slots = split_slots(ws, N)
+    assert [i for i in range(N) if slots[i] >= 0] == split, slots
+    check(f"bf16 varlen split schedule N{N} H{H} T{T} ckpt {ckpt}", x, got,
+          run_oracle(x, ckpt), TOL_BF16)
+
+
+def test_bf16_split_schedule_without_final_state():
+    # no S_final: the first segment's end state still reaches the walk
+    lengths = [64, 2048, 64, 64, 1, 64, 64, 64]
+    x = W.varlen_inputs(BASE, lengths, H=32, seed=32)
+    o, S, _ = run_gpu(x, want_state=False)
+    assert S is None
+    ro, _, _ = run_oracle(x)
+    report("bf16 varlen split schedule, no S_final", [("o", o, ro, (1,))], TOL_BF16)
+
+
+def test_bf16_split_schedule_chunk_budget():
+    # second segments are capped at 16384 / H chunks (256 at H = 64): the
+    # 30,000-token sequence (469 chunks, M = 118) keeps 213 in the fused
+    # kernel instead of 118. Inputs on the device; the oracle checks two
+    # heads of the long sequence and every head of the short ones.
+    lengths, H = [64, 64, 30000, 64], 64
+    x = W.varlen_inputs(BASE, lengths, H=H, seed=33, device=DEV)
+    N, T = len(lengths), sum(lengths)
+    nbytes = kda.kda_prefill_varlen_workspace_size(N, T, H, 128, 128, torch.bfloat16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    xd = dict(x)
+    xd["cu_seqlens"] = x["cu_seqlens"].to(DEV)
+    o, S, _ = kda.kda_prefill_varlen(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"],
+                                     xd["cu_seqlens"], xd["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    sp = ((3 * N + 3) * 4 + 255) & ~255
+    ints = ws[sp:sp + 12 * N].cpu().view(torch.int32).tolist()
+    assert ints[N:2 * N] == [64, 64, 213 * 64, 64]          # fused lengths
+    assert ints[2 * N:3 * N] == [-1, -1, 0, -1]              # the long one is split
+    cu = x["cu_seqlens"].tolist()
+    for i, heads in ((2, [5, 42]), (0, list(range(H))), (3, list(range(H)))):
+        a, b = cu[i], cu[i + 1]
+        sub = {n: x[n][a:b][:, heads].cpu() for n in ("q", "k", "v", "log_alpha", "beta")}
+        sub["S0"] = x["S0"][i:i + 1][:, heads].cpu()
+        sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32)
+        ro, rS, _ = run_oracle(sub)
+        report(f"split budget: sequence {i} ({b - a} tokens, heads {heads[:2]}..)",
+               [("o", o[a:b][:, heads].cpu(), ro, (1,)), ("S_final", S[i:i + 1][:, heads].cpu(), rS)],
+               TOL_BF16)
+
+
 def test_bf16_without_initial_state_or_checkpoints():
     x = W.varlen_inputs(BASE, [300, 5, 129], H=8, seed=22)
     x["S0"] = None
@@ -166,17 +238,22 @@ def test_varlen_config_full_size_sampled():
     o, S, Sc = run_gpu(x, ckpt_every=c.ckpt_every)
     cu = x["cu_seqlens"].tolist()
     ck0 = np.concatenate([[0], np.cumsum([n // c.ckpt_every for n in lengths])])
-    order = np.argsort(lengths)[:2]
-    for i in order:
+    order = np.argsort(lengths)
+    # the two shortest sequences on every head; the two longest (which the
+    # split schedule cuts between the fused kernel and the state walk) on
+    # two heads each, all tokens and checkpoints
+    for i, heads in [(i, None) for i in order[:2]] + [(i, [3, 29]) for i in order[-2:]]:
         a, b = cu[i], cu[i + 1]
-        sub = {n: x[n][a:b] for n in ("q", "k", "v", "log_alpha", "beta")}
-        sub["S0"] = x["S0"][i:i + 1]
+        hs = slice(None) if heads is None else heads
+        sub = {n: x[n][a:b][:, hs] for n in ("q", "k", "v", "log_alpha", "beta")}
+        sub["S0"] = x["S0"][i:i + 1][:, hs]
         sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32)
         ro, rS, rSc = run_oracle(sub, c.ckpt_every)
-        pairs = [("o", o[a:b], ro, (1,)), ("S_final", S[i:i + 1], rS)]
+        pairs = [("o", o[a:b][:, hs].cpu(), ro, (1,)), ("S_final", S[i:i + 1][:, hs].cpu(), rS)]
         if rSc.shape[0]:
-            pairs.append(("S_ckpt", Sc[ck0[i]:ck0[i + 1]], rSc))
-        report(f"varlen full size: sequence {i} ({b - a} tokens, all heads)", pairs, TOL_BF16)
+            pairs.append(("S_ckpt", Sc[ck0[i]:ck0[i + 1]][:, hs].cpu(), rSc))
+        what = "all heads" if heads is None else f"heads {heads}"
+        report(f"varlen full size: sequence {i} ({b - a} tokens, {what})", pairs, TOL_BF16)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
 
 

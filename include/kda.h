@@ -102,7 +102,9 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace kda_prefill_varlen needs for these sizes (never 0
  * for N, H > 0: it always holds the sequence table). Returns 0 for arguments
- * it would reject.
+ * it would reject. For bf16 with 256 or more sequence-heads and at most 1024
+ * sequences it also holds the split schedule's tables, end states and
+ * operand records (at most 16384 chunk-heads of 72,192 B: about 1.2 GB).
  */
 size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int dv,
                                          kda_dtype dtype, int chunk);
@@ -138,7 +140,11 @@ size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int 
  *   ws, ws_bytes  device workspace, 256-byte aligned, at least
  *            kda_prefill_varlen_workspace_size() bytes (required).
  * Outputs (o, S_final, S_ckpt, ws) must not overlap each other or an input.
- * The result for each sequence equals kda_prefill_fwd on that sequence alone.
+ * The result for each sequence equals kda_prefill_fwd on that sequence alone,
+ * up to rounding: with many sequence-heads (bf16, N * H >= 256), a sequence
+ * much longer than the rest runs its first chunks in the fused kernel and the
+ * others through the chunk-parallel prep and the state walk, decided on the
+ * device from the offsets, so that it does not set the call's length alone.
  */
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v,
                               const float* log_alpha, const float* beta,

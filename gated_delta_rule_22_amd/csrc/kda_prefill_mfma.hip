@@ -1424,7 +1424,10 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
 // their first segment, whose end state goes to sq1.mid); the other G per
 // head prepare the records of the second segments (table sq2), each a
 // consecutive share of that head's second-segment chunks. Both halves hold
-// the same LDS blocks, so the grid mixes them freely.
+// the same LDS blocks, so the grid mixes them freely. The prep shares are
+// issued from the numbering's end back to its start, so the records of the
+// first entries (the walk's first and longest chains) are written last and
+// are the likeliest still in the last-level cache when the walk reads them.
 template <bool CKPT>
 __global__ __launch_bounds__(512, 1) void prefill_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -1440,7 +1443,7 @@ __global__ __launch_bounds__(512, 1) void prefill_split_kernel(
                                ck_slots, Prologue{}, Epilogue{});
         return;
     }
-    const int p = blk - nfused, h = p / G, grp = p - h * G;
+    const int p = blk - nfused, grp = G - 1 - p / H, h = p % H;
     const int total2 = sq2.tab[2 * sq2.N + 1];
     const int cpw = (total2 + G - 1) / G;
     if (grp * cpw >= total2) return;                 // whole workgroup: uniform

@@ -136,33 +136,38 @@ __global__ __launch_bounds__(kTabThreads) void varlen_split_kernel(
     int* tab2 = out + 3 * N;
     int* lens2 = tab2 + 3 * n2 + 3;
     int* fin2 = lens2 + n2;
-    // taken candidates form a prefix of the candidates: entry j = pc - 1
+    // Entries of the second table go longest first (by second-segment
+    // chunks, ties by index), so the state walk starts its longest chains
+    // first; entry j's chunks follow those of entries 0 .. j-1.
+    const int nch2 = taken ? nch - m : 0;
+    key[i] = nch2;
+    __syncthreads();
+    int j = 0, c2 = 0, total2 = 0, nl = 0;
+    for (int u = 0; u < N; ++u) {
+        const int ku = key[u];
+        const bool ahead = ku > nch2 || (ku == nch2 && u < i);
+        j += ku > 0 && ahead;
+        c2 += ahead ? ku : 0;
+        total2 += ku;
+        nl += ku > 0;
+    }
     if (live) {
         lens1[i] = len1;
-        mslot[i] = taken ? pc - 1 : -1;
+        mslot[i] = taken ? j : -1;
     }
     if (taken) {
-        const int j = pc - 1;
         tab2[j] = st + m * C;
-        tab2[n2 + 1 + j] = before;
+        tab2[n2 + 1 + j] = c2;
         tab2[2 * n2 + 2 + j] = K > 0 ? tab[2 * N + 2 + i] + m * C / K : 0;
         lens2[j] = len - m * C;
         fin2[j] = i;
     }
-    // second-segment chunks actually taken: those of the last taken entry end it
-    key[i] = taken ? before + (nch - m) : 0;
-    __syncthreads();
-    int total2 = 0, nl = 0;
-    for (int u = 0; u < N; ++u) {
-        total2 = max(total2, key[u]);
-        nl += key[u] > 0;
-    }
-    for (int j = nl + i; j < n2; j += kTabThreads) {         // unused entries
-        tab2[j] = T;
-        tab2[n2 + 1 + j] = total2;
-        tab2[2 * n2 + 2 + j] = 0;
-        lens2[j] = 0;
-        fin2[j] = -1;
+    for (int e = nl + i; e < n2; e += kTabThreads) {         // unused entries
+        tab2[e] = T;
+        tab2[n2 + 1 + e] = total2;
+        tab2[2 * n2 + 2 + e] = 0;
+        lens2[e] = 0;
+        fin2[e] = -1;
     }
     if (i == 0) {
         tab2[n2] = T;

@@ -1281,14 +1281,15 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
         const int ck_every = CKPT ? sq.K / C : 1;   // chunks per checkpoint
         int ck_left = ck_every;                      // chunks until the next one
         int ck_slot = CKPT ? (int)sq.ckpt0(b) : 0;   // its slot
-        struct Ops { bf16x8 k[4]; f32x4 al[2]; };
+        // a_last of rows 32s .. 32s + 31: one dword per lane (lanes 32-63
+        // repeat 0-31), spread to the accumulator layout by lane shuffles,
+        // instead of 16-byte loads that return the same bytes to 16 lanes
+        struct Ops { bf16x8 k[4]; float al; };
         auto load = [&](Ops& x, int c) {
             const char* rp = rec(c);
 #pragma unroll
             for (int j = 0; j < 4; ++j) x.k[j] = op(rp, REC_KR + (2 * m0 + j) * OPB);
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                x.al[m] = *reinterpret_cast<const f32x4*>(rp + REC_AL + (16 * (m0 + m) + 4 * g) * 4);
+            x.al = *reinterpret_cast<const float*>(rp + REC_AL + (32 * s + (lane & 31)) * 4);
         };
         Ops sets[PF];
 #pragma unroll
@@ -1297,8 +1298,10 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
         walk(sets, [&](Ops& x, Ops& px, int c, auto) {
             lds_barrier();                                   // S_c ready
             load(px, c + PF - 1);
-            Sacc[0] *= x.al[0];
-            Sacc[1] *= x.al[1];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Sacc[m][i] *= __shfl(x.al, 16 * m + 4 * g + i);
             lds_barrier();                                   // U_c ready
             const bf16x8 UB0 = *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]);
             const bf16x8 UB1 = *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]);

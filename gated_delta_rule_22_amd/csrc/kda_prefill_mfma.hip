@@ -1459,17 +1459,15 @@ namespace {
 constexpr size_t DK_STATE_BYTES = size_t(128) * 128 * 4;   // one fp32 state
 }
 
-#ifndef KDA_PIECE_CHUNKS
-#define KDA_PIECE_CHUNKS 80
-#endif
 namespace {
 constexpr long kSplitBelowHeads = 128;   // fewer heads than this: prep + state kernels
 // Piecewise split path: fixed-length batches whose records would outgrow the
 // last-level cache run prep and state walk piece by piece along the
-// sequence, KDA_PIECE_CHUNKS chunks per sequence at a time (more when the
-// batch has few sequence-heads, so that a piece's prep still covers the GPU).
+// sequence, about kPieceWork chunk-heads at a time: 3072 records are 221.8 MB,
+// which the walk reads back from the 256 MB last-level cache (the prep reads
+// its inputs non-temporally to leave it to them).
 constexpr size_t kPieceAbove = size_t(192) << 20;
-constexpr long kPieceMinWork = 512;      // chunk-heads per piece, at least
+constexpr long kPieceWork = 3072;
 }
 
 bool prefill_mfma_supported(int dk, int dv, int chunk, long H) {
@@ -1487,8 +1485,7 @@ size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H) {
 long prefill_mfma_piece(long pairs, long nch_seq) {
     if (!prefill_mfma_split(pairs)) return 0;
     if ((size_t)pairs * (size_t)nch_seq * mf::REC_BYTES <= kPieceAbove) return 0;
-    long L = KDA_PIECE_CHUNKS;
-    while (L * pairs < kPieceMinWork) L *= 2;
+    const long L = std::max(1L, kPieceWork / pairs);
     return L < nch_seq ? L : 0;
 }
 

@@ -206,10 +206,12 @@ def test_split_path_regimes_alternate_within_workgroup():
 def test_piecewise_split_path_all_heads():
     # Few heads with records that would outgrow the last-level cache: the
     # split path runs prep and state walk piece by piece along the sequence
-    # (B1 H4 T65536: pieces of 160 chunks), the state carried in S_final.
+    # (about 3072 chunk-heads per piece; B1 H4 T65536: pieces of 768 and 256
+    # chunks), the state carried in S_final. The workspace holds one piece.
     c = W.PREFILL_CONFIGS["long"]
     x = W.prefill_inputs(c, B=1, T=65536, H=4, seed=31)
-    assert kda.kda_prefill_workspace_size(1, 65536, 4, 128, 128, torch.bfloat16) < 64 << 20
+    piece = 4 * 768 * 72192 + 4 * 128 * 128 * 4          # records + carried state
+    assert kda.kda_prefill_workspace_size(1, 65536, 4, 128, 128, torch.bfloat16) == piece
     o, S = gpu_prefill(to_dev(x))
     ro, rS = oracle_prefill(x)
     report("piecewise split path B1 H4 T65536", [("o", o, ro), ("S", S, rS)], TOL_BF16)
@@ -218,8 +220,8 @@ def test_piecewise_split_path_all_heads():
 @pytest.mark.parametrize("mode", ["S_final", "no_state", "in_place"])
 def test_piecewise_split_path_batch_ragged(mode):
     # Two sequences (strided windows of the batch), a carried S0 and a ragged
-    # last piece of one chunk of 33 tokens (801 chunks per sequence: five
-    # pieces of 160 and one); the state carried in S_final, in the workspace
+    # last piece ending in a chunk of 33 tokens (801 chunks per sequence:
+    # pieces of 768 and 33); the state carried in S_final, in the workspace
     # (no S_final wanted), or in S0 itself (S_final = S0).
     c = W.PREFILL_CONFIGS["batched"]
     T = 800 * 64 + 33

@@ -1630,8 +1630,13 @@ SplitPlan prefill_split_plan(int N, int T_total, int H, size_t base) {
     // split table is built by one workgroup of 1024 threads
     if ((long)N * H < 256 || N > 1024 || T_total <= 0) return p;
     // a split sequence has more than total * H / 256 chunks, so fewer than
-    // 256 / H of them exist; the prep's chunk map holds up to 127 entries
-    p.n2 = std::min(std::min(N, 127), (256 + H - 1) / H);
+    // 256 / H of them exist (none at 256 heads or more); the prep's chunk
+    // map holds up to 127 entries
+    p.n2 = std::min(std::min(N, 127), (256 + H - 1) / H - 1);
+    if (p.n2 <= 0) {
+        p.n2 = 0;
+        return p;
+    }
     const long nb = ((long)T_total + (long)N * (mf::C - 1)) / mf::C;   // chunks, at most
     // records of at most 16384 chunk-heads (1.18 GB)
     p.cap2 = (int)std::min(nb, std::max(64L, 16384L / H));

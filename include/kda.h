@@ -102,9 +102,10 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace kda_prefill_varlen needs for these sizes (never 0
  * for N, H > 0: it always holds the sequence table). Returns 0 for arguments
- * it would reject. For bf16 with 256 or more sequence-heads and at most 1024
- * sequences it also holds the split schedule's tables, end states and
- * operand records (at most 16384 chunk-heads of 72,192 B: about 1.2 GB).
+ * it would reject. For bf16 with 256 or more sequence-heads, fewer than 256
+ * heads and at most 1024 sequences it also holds the split schedule's
+ * tables, end states and operand records (at most 16384 chunk-heads of
+ * 72,192 B: about 1.2 GB).
  */
 size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int dv,
                                          kda_dtype dtype, int chunk);

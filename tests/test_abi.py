@@ -177,8 +177,10 @@ def test_varlen_workspace_query(lib):
     big = f(18, 65536, 32, 128, 128, 1, 64)
     assert rec < big < rec + (64 << 20)
     assert f(18, 65536, 32, 128, 128, 0, 64) == 256  # fp32: no split schedule
-    # more than 1024 sequences: table only
+    # more than 1024 sequences, or 256 heads or more (no sequence can exceed
+    # an even share): table only
     assert f(1025, 65536, 32, 128, 128, 1, 64) == (3 * 1025 + 3) * 4 + 255 & ~255
+    assert f(2, 65536, 256, 128, 128, 1, 64) == 256
 
 
 @no_gpu

@@ -114,6 +114,39 @@ def test_bf16_split_schedule_without_final_state():
     report("bf16 varlen split schedule, no S_final", [("o", o, ro, (1,))], TOL_BF16)
 
 
+def test_bf16_split_schedule_in_place():
+    # S_final = S0: the walk writes each split sequence's final state over
+    # its S0 row, which the fused kernel read in the launch before
+    lengths = [3000, 100, 0, 65, 2500] + [64] * 11
+    x = W.varlen_inputs(BASE, lengths, H=16, seed=34)
+    xd = to_dev(x)
+    S_io = xd["S0"].clone()
+    o, S, _ = kda.kda_prefill_varlen(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"],
+                                     xd["cu_seqlens"], S_io, S_final=S_io)
+    torch.cuda.synchronize()
+    assert S.data_ptr() == S_io.data_ptr()
+    ro, rS, _ = run_oracle(x)
+    report("bf16 varlen split schedule, S_final = S0", [("o", o, ro, (1,)), ("S_final", S, rS)],
+           TOL_BF16)
+
+
+def test_bf16_split_schedule_many_entries():
+    # H = 1, 300 sequences: the 100 of 16 chunks exceed the even share (M = 8)
+    # and are all split, so the second table has 100 entries (the prep's
+    # chunk map reads entries 64-99 from its second lane-distributed half)
+    lengths = [64, 1024, 64] * 100
+    x = W.varlen_inputs(BASE, lengths, H=1, seed=35)
+    N, T = len(lengths), sum(lengths)
+    nbytes = kda.kda_prefill_varlen_workspace_size(N, T, 1, 128, 128, torch.bfloat16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    got = run_gpu(x, ckpt_every=256, workspace=ws)
+    slots = split_slots(ws, N)
+    assert sorted(s for s in slots if s >= 0) == list(range(100))
+    assert [i for i in range(N) if slots[i] >= 0] == list(range(1, N, 3))
+    check(f"bf16 varlen split schedule, 100 split of {N}, H1", x, got, run_oracle(x, 256),
+          TOL_BF16)
+
+
 def test_bf16_split_schedule_chunk_budget():
     # second segments are capped at 16384 / H chunks (256 at H = 64): the
     # 30,000-token sequence (469 chunks, M = 118) keeps 213 in the fused

@@ -1430,7 +1430,8 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
 // the same LDS blocks, so the grid mixes them freely. The prep shares are
 // issued from the numbering's end back to its start, so the records of the
 // first entries (the walk's first and longest chains) are written last and
-// are the likeliest still in the last-level cache when the walk reads them.
+// are the likeliest still in the last-level cache when the walk reads them;
+// the prep reads its inputs non-temporally to leave that cache to them.
 template <bool CKPT>
 __global__ __launch_bounds__(512, 1) void prefill_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -1450,7 +1451,7 @@ __global__ __launch_bounds__(512, 1) void prefill_split_kernel(
     const int total2 = sq2.tab[2 * sq2.N + 1];
     const int cpw = (total2 + G - 1) / G;
     if (grp * cpw >= total2) return;                 // whole workgroup: uniform
-    prep_body<true, 0, false>(sm, sV, h, grp * cpw, cpw, q, k, v, la, beta, ws, sq2, H, nrec,
+    prep_body<true, 0, true>(sm, sV, h, grp * cpw, cpw, q, k, v, la, beta, ws, sq2, H, nrec,
                               Prologue{});
 }
 

@@ -217,6 +217,19 @@ def test_piecewise_split_path_all_heads():
     report("piecewise split path B1 H4 T65536", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
+def test_piecewise_split_path_many_heads():
+    # 100 sequence-heads (below the fused path's 128): the piece is
+    # 3072 / 100 = 30 chunks, so B1 H100 T2560 (40 chunks, 289 MB of records)
+    # runs a piece of 30 and a last one of 10, all heads checked
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=1, T=2560, H=100, seed=33)
+    piece = 100 * 30 * 72192 + 100 * 128 * 128 * 4
+    assert kda.kda_prefill_workspace_size(1, 2560, 100, 128, 128, torch.bfloat16) == piece
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report("piecewise split path B1 H100 T2560", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
 @pytest.mark.parametrize("mode", ["S_final", "no_state", "in_place"])
 def test_piecewise_split_path_batch_ragged(mode):
     # Two sequences (strided windows of the batch), a carried S0 and a ragged

@@ -43,37 +43,22 @@ bool mul_ok(size_t& acc, size_t x) {
     return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* kda_status_string(kda_status s) {
-    switch (s) {
-        case KDA_OK: return "ok";
-        case KDA_ERR_INVALID_ARG: return "invalid argument";
-        case KDA_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
-        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
-        case KDA_ERR_HIP: return "HIP launch failed";
-        case KDA_ERR_SCRATCH:
-            return "the call needs more device scratch than the library's static buffer "
-                   "holds (kda_prefill_fwd_noalloc; use kda_prefill_fwd with a workspace)";
-    }
-    return "unknown status";
-}
-
-size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dtype,
-                                  int chunk) {
+// kda_prefill_fwd with the workspace capped at max_ws bytes: the piecewise
+// split path then runs pieces short enough for one to fit (kda_prefill_fwd
+// itself passes no cap; the allocation-free entry point its static array).
+size_t prefill_workspace_capped(int B, int T, int H, int dk, int dv, kda_dtype dtype, int chunk,
+                                size_t max_ws) {
     if (B <= 0 || T <= 0 || H <= 0 || dtype != KDA_BF16) return 0;
     if (!kda::prefill_mfma_supported(dk, dv, chunk, H)) return 0;
-    return kda::prefill_mfma_workspace_fixed(B, H, ((long)T + kChunk - 1) / kChunk);
+    return kda::prefill_mfma_workspace_fixed(B, H, ((long)T + kChunk - 1) / kChunk, max_ws);
 }
 
-kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
-                           const float* log_alpha, const float* beta,
-                           const float* S0, void* o, float* S_final,
-                           int B, int T, int H, int dk, int dv,
-                           kda_dtype dtype, int chunk,
-                           void* ws, size_t ws_bytes, void* stream) {
+kda_status prefill_fwd_capped(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta,
+                              const float* S0, void* o, float* S_final,
+                              int B, int T, int H, int dk, int dv,
+                              kda_dtype dtype, int chunk,
+                              void* ws, size_t ws_bytes, size_t max_ws, void* stream) {
     if (B < 0 || T < 0 || H < 0) return KDA_ERR_INVALID_ARG;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
@@ -93,7 +78,7 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
     const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_final};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
-    const size_t ws_need = kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk);
+    const size_t ws_need = prefill_workspace_capped(B, T, H, dk, dv, dtype, chunk, max_ws);
     if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need)) return KDA_ERR_WORKSPACE;
     if (ws_need > 0 && !aligned16(ws)) return KDA_ERR_INVALID_ARG;
 
@@ -125,13 +110,46 @@ kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
         bool epi_done;
         e = kda::launch_prefill_mfma(q, k, v, log_alpha, beta, S0, o, S_final, sq, H, (int)nch,
                                      ws, nullptr, 0, 0, kda::Prologue{}, kda::Epilogue{},
-                                     &epi_done, st);
+                                     &epi_done, st, max_ws);
     } else {
         e = kda::launch_prefill_generic(dtype == KDA_BF16, q, k, v, log_alpha, beta, S0, o,
                                         S_final, sq, H, dk, dv, chunk ? chunk : 64, nullptr, 0,
                                         0, kda::Prologue{}, st);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP launch failed";
+        case KDA_ERR_SCRATCH:
+            return "the call needs more device scratch than the library's static buffer "
+                   "holds (kda_prefill_fwd_noalloc; use kda_prefill_fwd with a workspace)";
+    }
+    return "unknown status";
+}
+
+size_t kda_prefill_workspace_size(int B, int T, int H, int dk, int dv, kda_dtype dtype,
+                                  int chunk) {
+    return prefill_workspace_capped(B, T, H, dk, dv, dtype, chunk, SIZE_MAX);
+}
+
+kda_status kda_prefill_fwd(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* S0, void* o, float* S_final,
+                           int B, int T, int H, int dk, int dv,
+                           kda_dtype dtype, int chunk,
+                           void* ws, size_t ws_bytes, void* stream) {
+    return prefill_fwd_capped(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, dk, dv, dtype,
+                              chunk, ws, ws_bytes, SIZE_MAX, stream);
 }
 
 size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int dv,
@@ -501,7 +519,11 @@ kda_status kda_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
                                    const float* S0, void* o, float* S_final,
                                    int B, int T, int H, int dk, int dv,
                                    kda_dtype dtype, int chunk, void* stream) {
-    const size_t need = kda_prefill_workspace_size(B, T, H, dk, dv, dtype, chunk);
+    // the workspace capped at the array: a long few-head call runs its
+    // pieces short enough for one to fit (slower than with the usual pieces,
+    // which keep the records of 3072 chunk-heads in the last-level cache)
+    const size_t need = prefill_workspace_capped(B, T, H, dk, dv, dtype, chunk,
+                                                 KDA_NOALLOC_SCRATCH_BYTES);
     if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
     void* ws = nullptr;
     if (need > 0) {
@@ -511,8 +533,9 @@ kda_status kda_prefill_fwd_noalloc(const void* q, const void* k, const void* v,
     // every other rule (and every launch) is kda_prefill_fwd's; its kernels
     // write each record of the workspace before they read it, so the array
     // needs no clearing between calls
-    return kda_prefill_fwd(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, dk, dv, dtype,
-                           chunk, ws, need > 0 ? KDA_NOALLOC_SCRATCH_BYTES : 0, stream);
+    return prefill_fwd_capped(q, k, v, log_alpha, beta, S0, o, S_final, B, T, H, dk, dv, dtype,
+                              chunk, ws, need > 0 ? KDA_NOALLOC_SCRATCH_BYTES : 0,
+                              KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

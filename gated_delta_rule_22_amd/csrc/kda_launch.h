@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 #include "kda_common.h"
 
@@ -73,14 +74,20 @@ size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H);
 // Fixed-length batches (B sequences of nch_seq chunks): the workspace of the
 // split path, which for long sequences holds one piece of records (the
 // launcher then walks the sequence piece by piece) plus a carried state.
-size_t prefill_mfma_workspace_fixed(int B, int H, long nch_seq);
-// Chunks per sequence of one piece of the piecewise split path, 0 = none.
-long prefill_mfma_piece(long pairs, long nch_seq);
+// max_ws caps it: pieces shrink until one fits (SIZE_MAX: not even a piece
+// of one chunk fits).
+size_t prefill_mfma_workspace_fixed(int B, int H, long nch_seq, size_t max_ws = SIZE_MAX);
+// Chunks per sequence of one piece of the piecewise split path, 0 = none,
+// -1 = no piece fits max_ws.
+long prefill_mfma_piece(long pairs, long nch_seq, size_t max_ws = SIZE_MAX);
+// max_ws: the workspace bound the call's workspace size was computed with
+// (prefill_mfma_workspace_fixed), which fixes the piece length.
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* gate,
                                const float* beta, const float* S0, void* o, float* S_final,
                                const SeqLayout& sq, int H, int nch_all, void* ws,
                                float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
-                               const Epilogue& ep, bool* epi_done, hipStream_t st);
+                               const Epilogue& ep, bool* epi_done, hipStream_t st,
+                               size_t max_ws = SIZE_MAX);
 
 // Split schedule of a packed call with many sequence-heads (N * H >= 256,
 // N <= 1024): workspace layout after the sequence table (at byte `base`):

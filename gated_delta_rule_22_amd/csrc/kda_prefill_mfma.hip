@@ -1483,16 +1483,26 @@ size_t prefill_mfma_workspace(long pairs, size_t nch_all, int H) {
     return (size_t)H * nch_all * mf::REC_BYTES;
 }
 
-long prefill_mfma_piece(long pairs, long nch_seq) {
+long prefill_mfma_piece(long pairs, long nch_seq, size_t max_ws) {
     if (!prefill_mfma_split(pairs)) return 0;
-    if ((size_t)pairs * (size_t)nch_seq * mf::REC_BYTES <= kPieceAbove) return 0;
-    const long L = std::max(1L, kPieceWork / pairs);
+    const size_t rec = (size_t)pairs * mf::REC_BYTES;        // one chunk of every sequence
+    const size_t state = (size_t)pairs * DK_STATE_BYTES;
+    long L = (size_t)nch_seq * rec > kPieceAbove ? std::max(1L, kPieceWork / pairs) : nch_seq;
+    // the workspace holds the whole call's records, or one piece of them and
+    // the carried state: pieces shrink until that fits max_ws
+    const size_t need = L >= nch_seq ? (size_t)nch_seq * rec : (size_t)L * rec + state;
+    if (need > max_ws) {
+        const size_t room = max_ws > state ? max_ws - state : 0;
+        L = std::min(L, (long)std::min(room / rec, (size_t)nch_seq));
+        if (L < 1) return -1;
+    }
     return L < nch_seq ? L : 0;
 }
 
-size_t prefill_mfma_workspace_fixed(int B, int H, long nch_seq) {
+size_t prefill_mfma_workspace_fixed(int B, int H, long nch_seq, size_t max_ws) {
     const long pairs = (long)B * H;
-    const long L = prefill_mfma_piece(pairs, nch_seq);
+    const long L = prefill_mfma_piece(pairs, nch_seq, max_ws);
+    if (L < 0) return SIZE_MAX;
     if (L == 0) return prefill_mfma_workspace(pairs, (size_t)B * (size_t)nch_seq, H);
     // one piece of records, then the carried state (used when the caller
     // wants no S_final)
@@ -1573,7 +1583,7 @@ hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const vo
                            const float* beta, const float* S0, void* o, float* S_final,
                            const SeqLayout& sq, int H, int nch_all, void* ws, float* S_ckpt,
                            int ck_slots, const Prologue& pr, const Epilogue& ep,
-                           bool* epi_done, hipStream_t st)
+                           bool* epi_done, size_t max_ws, hipStream_t st)
 {
     const long pairs = (long)sq.N * H;
     const bool ck = S_ckpt != nullptr && sq.K > 0 && ck_slots > 0;
@@ -1591,7 +1601,8 @@ hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const vo
         return hipGetLastError();
     }
     // few sequence-heads, long sequences: prep and state walk piece by piece
-    const long L = sq.tab ? 0 : prefill_mfma_piece(pairs, (long)nch_all / sq.N);
+    const long L = sq.tab ? 0 : prefill_mfma_piece(pairs, (long)nch_all / sq.N, max_ws);
+    if (L < 0) return hipErrorInvalidValue;
     if (L > 0) return launch_mfma_pieces<PRO>(q, k, v, gate, beta, S0, o, S_final, sq, H,
                                               nch_all, ws, L, pr, st);
     // few sequence-heads: chunk-parallel prep, then the state walk
@@ -1696,12 +1707,13 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                const float* beta, const float* S0, void* o, float* S_final,
                                const SeqLayout& sq, int H, int nch_all, void* ws,
                                float* S_ckpt, int ck_slots, int pro, const Prologue& pr,
-                               const Epilogue& ep, bool* epi_done, hipStream_t st)
+                               const Epilogue& ep, bool* epi_done, hipStream_t st,
+                               size_t max_ws)
 {
 #define KDA_PRO_CASE(P)                                                                     \
     case P:                                                                                 \
         return launch_mfma_pro<P>(q, k, v, gate, beta, S0, o, S_final, sq, H, nch_all, ws,  \
-                                  S_ckpt, ck_slots, pr, ep, epi_done, st);
+                                  S_ckpt, ck_slots, pr, ep, epi_done, max_ws, st);
     switch (pro) {
         KDA_PRO_CASE(0)
         KDA_PRO_CASE(kGateBounded)

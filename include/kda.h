@@ -259,9 +259,14 @@ kda_status kda_decode_layer(const void* q, const void* k, const void* v, const v
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, which instead lives in a static
  * device array inside the library, KDA_NOALLOC_SCRATCH_BYTES (80 MiB) on each
- * GPU the library runs on, held until the process ends. Calls that need more
- * (kda_prefill_workspace_size() above that) return KDA_ERR_SCRATCH and launch
- * nothing; 16 heads of 4096 tokens need 73.9 MB. The call itself allocates
+ * GPU the library runs on, held until the process ends. A call whose usual
+ * workspace (kda_prefill_workspace_size()) is larger runs the few-head path
+ * in pieces short enough for one piece's records to fit the array: the same
+ * kernels on the same chunks, so the results are those of kda_prefill_fwd,
+ * at some speed (the usual pieces keep the records of 3072 chunk-heads,
+ * 222 MB, in the last-level cache). A call that could not fit even one chunk
+ * per piece returns KDA_ERR_SCRATCH and launches nothing; with fewer than
+ * 128 sequence-heads on that path, none does. The call itself allocates
  * nothing: no hipMalloc, no hipFree, no allocating library routine.
  * Every call on one GPU shares that GPU's array, and it keeps the last
  * call's contents: calls that overlap on one GPU (on different streams, or

@@ -1183,25 +1183,34 @@ constexpr int PF = 4;   // operand sets in flight per wave
 
 // With CKPT the S waves also store the state after every sq.K tokens of the
 // sequence to checkpoint slot sq.ckpt0(i) + j - 1 (slots >= ck_slots are dropped).
-template <bool CKPT>
-__global__ __launch_bounds__(832, 1) void prefill_state_kernel(
+// NCT: 16-column tiles per workgroup (1 or 2). With 2, each workgroup covers
+// 32 value columns and applies every operand it fetches to both tiles, so a
+// head takes four workgroups instead of eight: half the workgroups for the
+// same call, each fetching about the same bytes per chunk. That form runs
+// without the L2-touch wave (twelve waves, up to 168 registers per lane: the
+// two tiles' accumulators and operand sets do not fit in 128).
+template <bool CKPT, int NCT>
+__global__ __launch_bounds__(NCT == 1 ? 832 : 768, 1) void prefill_state_kernel(
     const char* __restrict__ ws, const float* S0, bf16* __restrict__ o, float* S_final,
     SeqLayout sq, int H, int BH, int nch_all, float* __restrict__ S_ckpt, int ck_slots)
 {
     using namespace mf;
-    __shared__ bf16x8 sSB[4][64];        // S as four B operands (32-deep steps)
-    __shared__ bf16x4 sUB[2][64][2];     // U as two B operands, halves by token tile
-    __shared__ __attribute__((aligned(16))) bf16 sO[4][16 * 16];   // output tiles, token-major
+    static_assert(NCT == 1 || NCT == 2, "16 or 32 value columns per workgroup");
+    constexpr int NT = 8 / NCT;            // workgroups per head
+    constexpr int CW = 16 * NCT;           // value columns per workgroup
+    __shared__ bf16x8 sSB[NCT][4][64];     // S as four B operands (32-deep steps), per tile
+    __shared__ bf16x4 sUB[NCT][2][64][2];  // U as two B operands, halves by token tile
+    __shared__ __attribute__((aligned(16))) bf16 sO[4][16 * CW];   // output tiles, token-major
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 4, r = lane & 15;
-    const int grp = blockIdx.x >> 6;
+    const int grp = blockIdx.x / (8 * NT);
     const int bh = grp * 8 + (blockIdx.x & 7);
-    const int ct = (blockIdx.x >> 3) & 7;          // value column tile
+    const int ct = (blockIdx.x >> 3) % NT;         // value column tile of CW columns
     if (bh >= BH) return;                          // whole workgroup: uniform
     const int b = bh / H, h = bh - b * H;          // sequence b, head h
     if (sq.fin && sq.fin[b] < 0) return;           // unused entry of a split schedule
-    const int ncol = 16 * ct + r;
+    auto ncol = [&](int u) { return CW * ct + 16 * u + r; };
     const long tok0 = sq.start(b);
     const int T = sq.len(b);
     const int nchunks = (T + C - 1) / C;
@@ -1242,23 +1251,28 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
         // ---- U = U0 - W S, token tile I (fetches in phase 2, PF ahead) ----
         __builtin_amdgcn_s_setprio(2);
         const int I = wave;
-        struct Ops { bf16x8 w[4]; uint2 u0; };
+        struct Ops { bf16x8 w[4]; uint2 u0[NCT]; };
         auto load = [&](Ops& x, int c) {
             const char* rp = rec(c);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) x.w[kk] = op(rp, REC_NW + (I * 4 + kk) * OPB);
-            x.u0 = *reinterpret_cast<const uint2*>(rp + REC_U0 + ((I * 8 + ct) * 64 + lane) * 8);
+#pragma unroll
+            for (int u = 0; u < NCT; ++u)
+                x.u0[u] = *reinterpret_cast<const uint2*>(rp + REC_U0 + ((I * 8 + NCT * ct + u) * 64 + lane) * 8);
         };
         Ops sets[PF];
 #pragma unroll
         for (int k = 0; k < PF; ++k) load(sets[k], k);
         walk(sets, [&](Ops& x, Ops&, int c, auto) {
             lds_barrier();                                   // S_c ready
-            const f32x2 lo = unpack2(x.u0.x), hi = unpack2(x.u0.y);
-            f32x4 acc = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mma32(x.w[kk], sSB[kk][lane], acc);
-            sUB[I >> 1][lane][I & 1] = __builtin_convertvector(acc, bf16x4);
+            for (int u = 0; u < NCT; ++u) {
+                const f32x2 lo = unpack2(x.u0[u].x), hi = unpack2(x.u0[u].y);
+                f32x4 acc = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mma32(x.w[kk], sSB[u][kk][lane], acc);
+                sUB[u][I >> 1][lane][I & 1] = __builtin_convertvector(acc, bf16x4);
+            }
             lds_barrier();                                   // U_c ready
             load(x, c + PF);
         });
@@ -1267,16 +1281,19 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
         //      (fetches in phase 1, PF - 1 ahead) ----
         __builtin_amdgcn_s_setprio(2);
         const int s = wave - 4, m0 = 2 * s;
-        f32x4 Sacc[2];
-        if (S0) {
+        f32x4 Sacc[NCT][2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+        for (int u = 0; u < NCT; ++u) {
+            if (S0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Sacc[m][i] = S0[sbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol];
-        } else {
-            Sacc[0] = zero4();
-            Sacc[1] = zero4();
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Sacc[u][m][i] = S0[sbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol(u)];
+            } else {
+                Sacc[u][0] = zero4();
+                Sacc[u][1] = zero4();
+            }
         }
         const int ck_every = CKPT ? sq.K / C : 1;   // chunks per checkpoint
         int ck_left = ck_every;                      // chunks until the next one
@@ -1294,56 +1311,70 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
         Ops sets[PF];
 #pragma unroll
         for (int k = 0; k < PF - 1; ++k) load(sets[k], k);
-        sSB[s][lane] = pack8(Sacc[0], Sacc[1]);
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) sSB[u][s][lane] = pack8(Sacc[u][0], Sacc[u][1]);
         walk(sets, [&](Ops& x, Ops& px, int c, auto) {
             lds_barrier();                                   // S_c ready
             load(px, c + PF - 1);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Sacc[m][i] *= __shfl(x.al, 16 * m + 4 * g + i);
-            lds_barrier();                                   // U_c ready
-            const bf16x8 UB0 = *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]);
-            const bf16x8 UB1 = *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]);
+                for (int i = 0; i < 4; ++i) {
+                    const float a = __shfl(x.al, 16 * m + 4 * g + i);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                Sacc[m] = mma32(x.k[2 * m], UB0, Sacc[m]);
-                Sacc[m] = mma32(x.k[2 * m + 1], UB1, Sacc[m]);
+                    for (int u = 0; u < NCT; ++u) Sacc[u][m][i] *= a;
+                }
+            lds_barrier();                                   // U_c ready
+#pragma unroll
+            for (int u = 0; u < NCT; ++u) {
+                const bf16x8 UB0 = *reinterpret_cast<const bf16x8*>(&sUB[u][0][lane][0]);
+                const bf16x8 UB1 = *reinterpret_cast<const bf16x8*>(&sUB[u][1][lane][0]);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    Sacc[u][m] = mma32(x.k[2 * m], UB0, Sacc[u][m]);
+                    Sacc[u][m] = mma32(x.k[2 * m + 1], UB1, Sacc[u][m]);
+                }
+                sSB[u][s][lane] = pack8(Sacc[u][0], Sacc[u][1]);
             }
-            sSB[s][lane] = pack8(Sacc[0], Sacc[1]);
             if (CKPT && --ck_left == 0) {                   // checkpoint after chunk c
                 ck_left = ck_every;
                 if ((c + 1) * C <= T && ck_slot < ck_slots) {
-                    float* dst = S_ckpt + ((size_t)ck_slot * H + h) * DK * 128 +
-                                 (16 * m0 + 4 * g) * 128 + ncol;
 #pragma unroll
-                    for (int m = 0; m < 2; ++m)
+                    for (int u = 0; u < NCT; ++u) {
+                        float* dst = S_ckpt + ((size_t)ck_slot * H + h) * DK * 128 +
+                                     (16 * m0 + 4 * g) * 128 + ncol(u);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) dst[(16 * m + i) * 128] = Sacc[m][i];
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) dst[(16 * m + i) * 128] = Sacc[u][m][i];
+                    }
                 }
                 ++ck_slot;
             }
         });
         if (S_final) {
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int u = 0; u < NCT; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S_final[fbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol] = Sacc[m][i];
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S_final[fbase + (size_t)(16 * (m0 + m) + 4 * g + i) * 128 + ncol(u)] = Sacc[u][m][i];
         }
     } else if (wave == 12) {
         // ---- L2 prefetch (launched only for workspaces that stream from HBM):
-        //      this workgroup's eighth of the record eight chunks ahead, one
+        //      this workgroup's share of the record eight chunks ahead, one
         //      dword per 128-byte line, so that the role waves of the head's
-        //      eight column tiles (one XCD, one L2) hit L2 ----
+        //      column tiles (one XCD, one L2) hit L2 ----
         constexpr int kAhead = PF + 2;
-        constexpr int kSlice = REC_BYTES / 8;
-        uint32_t ring[3][2] = {};
+        constexpr int kSlice = REC_BYTES / NT;
+        constexpr int kTouch = 2 * NCT;             // lines per lane (64 x 128 B each)
+        uint32_t ring[3][kTouch] = {};
         uint32_t acc = 0;
-        auto touch = [&](uint32_t (&dst)[2], int c) {
+        auto touch = [&](uint32_t (&dst)[kTouch], int c) {
             const char* rp = rec(c);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < kTouch; ++u) {
                 const int off = min(ct * kSlice + (u * 64 + lane) * 128, REC_BYTES - 4);
                 dst[u] = *reinterpret_cast<const uint32_t*>(rp + off);
             }
@@ -1355,7 +1386,8 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
             for (int k = 0; k < 3; ++k) {
                 if (c + k < nchunks) {
                     lds_barrier();                           // S_c ready
-                    acc ^= ring[(k + 2) % 3][0] ^ ring[(k + 2) % 3][1];   // oldest set: long arrived
+#pragma unroll
+                    for (int u = 0; u < kTouch; ++u) acc ^= ring[(k + 2) % 3][u];   // oldest set: long arrived
                     touch(ring[(k + 2) % 3], c + k + kAhead + 2);
                     lds_barrier();                           // U_c ready
                 }
@@ -1376,10 +1408,11 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
             x.m0 = op(rp, REC_M + I * OPB);
             if (I >= 2) x.m1 = op(rp, REC_M + (I + 2) * OPB);
         };
-        // the tile leaves through LDS so that each lane stores 4 columns of
-        // one token (8 bytes) instead of 4 tokens of one column
+        // the tile leaves through LDS so that each lane stores 4 * NCT
+        // columns of one token (8 * NCT bytes) instead of 4 tokens of one column
         bf16* tile = sO[I];
-        const int tt = lane >> 2, tc = 4 * (lane & 3);
+        constexpr int LC = 4 * NCT;                  // columns per lane in the store
+        const int tt = lane >> 2, tc = LC * (lane & 3);
         // separate loops for the two fetch phases, so that each has one
         // load pattern the compiler can count across iterations
         auto run = [&](auto early) {
@@ -1392,18 +1425,24 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
                 // chunk freed, so they drain while this wave computes
                 lds_barrier();                               // S_c ready
                 if (kEarly) load(px, c + PF - 1);
-                f32x4 Oa = zero4(), Ob = zero4();
-                Oa = mma32(x.q[0], sSB[0][lane], Oa);
-                Ob = mma32(x.q[1], sSB[1][lane], Ob);
-                Oa = mma32(x.q[2], sSB[2][lane], Oa);
-                Ob = mma32(x.q[3], sSB[3][lane], Ob);
+                f32x4 Oa[NCT], Ob[NCT];
+#pragma unroll
+                for (int u = 0; u < NCT; ++u) {
+                    Oa[u] = mma32(x.q[0], sSB[u][0][lane], zero4());
+                    Ob[u] = mma32(x.q[1], sSB[u][1][lane], zero4());
+                    Oa[u] = mma32(x.q[2], sSB[u][2][lane], Oa[u]);
+                    Ob[u] = mma32(x.q[3], sSB[u][3][lane], Ob[u]);
+                }
                 lds_barrier();                               // U_c ready
                 if (!kEarly) load(px, c + PF - 1);
-                f32x4 O = mma32(x.m0, *reinterpret_cast<const bf16x8*>(&sUB[0][lane][0]), Oa);
-                if (I >= 2) Ob = mma32(x.m1, *reinterpret_cast<const bf16x8*>(&sUB[1][lane][0]), Ob);
-                O += Ob;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tile[(4 * g + e) * 16 + r] = (bf16)O[e];
+                for (int u = 0; u < NCT; ++u) {
+                    f32x4 O = mma32(x.m0, *reinterpret_cast<const bf16x8*>(&sUB[u][0][lane][0]), Oa[u]);
+                    if (I >= 2) Ob[u] = mma32(x.m1, *reinterpret_cast<const bf16x8*>(&sUB[u][1][lane][0]), Ob[u]);
+                    O += Ob[u];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tile[(4 * g + e) * CW + 16 * u + r] = (bf16)O[e];
+                }
                 lds_fence_wave();
                 // In a ragged last chunk, rows past the sequence end repeat the
                 // tile's last real row (same data, same address); a tile wholly
@@ -1411,9 +1450,17 @@ __global__ __launch_bounds__(832, 1) void prefill_state_kernel(
                 const int nt = T - c * C;
                 if (decltype(full)::value || 16 * I < nt) {
                     const int t = decltype(full)::value ? 16 * I + tt : min(16 * I + tt, nt - 1);
-                    const uint2 v = *reinterpret_cast<const uint2*>(&tile[(t - 16 * I) * 16 + tc]);
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(o + (((size_t)tok0 + (size_t)c * C + t) * H + h) * 128 + 16 * ct + tc));
+                    bf16* dst = o + (((size_t)tok0 + (size_t)c * C + t) * H + h) * 128 + CW * ct + tc;
+                    const bf16* src = &tile[(t - 16 * I) * CW + tc];
+                    if constexpr (NCT == 1) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(src);
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(dst));
+                    } else {
+                        const uint4 v = *reinterpret_cast<const uint4*>(src);
+                        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+                    }
                 }
             });
         };
@@ -1524,6 +1571,28 @@ auto fused_kernel_for(bool ck, bool epi) {
         return prefill_fused_kernel<NW, false, PRO>;
 }
 
+// Column tiles per state-walk workgroup: 16-column tiles put 8 workgroups
+// on a sequence-head; when the walk's sequence-heads need more than one
+// round of workgroups on the 256 compute units that way, 32-column tiles
+// (4 per sequence-head) halve the rounds, at a higher time per chunk.
+int state_tiles(long pairs) { return pairs * 8 > 256 ? 2 : 1; }
+
+// State walk of `pairs` sequence-heads: groups of 8 sequence-heads, each on
+// 8 / nct workgroups of 16 * nct value columns; the workgroups of one
+// sequence-head have block ids equal mod 8 (one XCD, one L2).
+hipError_t launch_state(bool ck, int nct, unsigned threads, const char* ws, const float* S0,
+                        bf16* o, float* S_final, const SeqLayout& sq, int H, long pairs,
+                        int nch_all, float* S_ckpt, int ck_slots, hipStream_t st)
+{
+    const long groups = (pairs + 7) / 8;
+    const dim3 grid((unsigned)(groups * 64 / nct)), block(nct == 2 ? 768u : threads);
+    auto kern = nct == 2 ? (ck ? prefill_state_kernel<true, 2> : prefill_state_kernel<false, 2>)
+                         : (ck ? prefill_state_kernel<true, 1> : prefill_state_kernel<false, 1>);
+    hipLaunchKernelGGL(kern, grid, block, 0, st, ws, S0, o, S_final, sq, H, (int)pairs, nch_all,
+                       S_ckpt, ck_slots);
+    return hipGetLastError();
+}
+
 // Piecewise split path (fixed-length batch, sq.tab == nullptr): for each
 // piece of L chunks of every sequence, the prep kernel writes its records
 // (one piece of the workspace, reused) and the state kernel walks them,
@@ -1545,7 +1614,7 @@ hipError_t launch_mfma_pieces(const void* q, const void* k, const void* v, const
     // the records were just written and sit in the last-level cache: no
     // L2-touch wave (it measured slower here)
     const unsigned threads = 768u;
-    const long groups = (pairs + 7) / 8;
+    const int nct = state_tiles(pairs);
     for (long c0 = 0; c0 < nch_seq; c0 += L) {
         const long Lc = std::min(L, nch_seq - c0);
         const long t0 = c0 * mf::C;
@@ -1569,10 +1638,8 @@ hipError_t launch_mfma_pieces(const void* q, const void* k, const void* v, const
                            0, st, qp, kp, vp, gp, bp, rec, sp, H, cpw, nch_piece, pr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(prefill_state_kernel<false>, dim3((unsigned)(groups * 64)), dim3(threads),
-                           0, st, (const char*)rec, c0 == 0 ? S0 : (const float*)carry, op, carry,
-                           sp, H, (int)pairs, nch_piece, (float*)nullptr, 0);
-        e = hipGetLastError();
+        e = launch_state(false, nct, threads, (const char*)rec, c0 == 0 ? S0 : (const float*)carry,
+                         op, carry, sp, H, pairs, nch_piece, nullptr, 0, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1623,15 +1690,12 @@ hipError_t launch_mfma_pro(const void* q, const void* k, const void* v, const vo
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const long groups = (pairs + 7) / 8;   // 8 pairs x 8 column tiles per group of 64 blocks
     // A workspace that outgrows the last-level cache (256 MB) streams from
     // HBM: add the L2 prefetch wave (thirteenth wave) for it.
     const size_t ws_bytes = prefill_mfma_workspace(pairs, (size_t)nch_all, H);
     const unsigned threads = ws_bytes > (size_t(128) << 20) ? 832u : 768u;
-    hipLaunchKernelGGL(ck ? prefill_state_kernel<true> : prefill_state_kernel<false>,
-                       dim3((unsigned)(groups * 64)), dim3(threads), 0, st, (const char*)ws, S0,
-                       (bf16*)o, S_final, sq, H, (int)pairs, nch_all, S_ckpt, ck_slots);
-    return hipGetLastError();
+    return launch_state(ck, state_tiles(pairs), threads, (const char*)ws, S0, (bf16*)o, S_final,
+                        sq, H, pairs, nch_all, S_ckpt, ck_slots, st);
 }
 
 }  // namespace
@@ -1692,15 +1756,14 @@ hipError_t launch_prefill_split(const void* q, const void* k, const void* v, con
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long BH2 = (long)n2 * H;
-    const long groups = (BH2 + 7) / 8;
     // records that may outgrow half the last-level cache: L2-touch wave
     const size_t rec_bytes = (size_t)H * plan.cap2 * mf::REC_BYTES;
     const unsigned threads = rec_bytes > (size_t(128) << 20) ? 832u : 768u;
-    hipLaunchKernelGGL(ck ? prefill_state_kernel<true> : prefill_state_kernel<false>,
-                       dim3((unsigned)(groups * 64)), dim3(threads), 0, st, (const char*)rec,
-                       (const float*)mid, (bf16*)o, S_final, sq2, H, (int)BH2, plan.cap2, S_ckpt,
-                       ck_slots);
-    return hipGetLastError();
+    // column tiles as for two split sequences (how many entries the device
+    // takes is not known here; entries are ordered longest first)
+    const int nct = state_tiles((long)std::min(n2, 2) * H);
+    return launch_state(ck, nct, threads, (const char*)rec, (const float*)mid, (bf16*)o, S_final,
+                        sq2, H, BH2, plan.cap2, S_ckpt, ck_slots, st);
 }
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* gate,

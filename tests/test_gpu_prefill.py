@@ -230,6 +230,17 @@ def test_piecewise_split_path_many_heads():
     report("piecewise split path B1 H100 T2560", [("o", o, ro), ("S", S, rS)], TOL_BF16)
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 48, 333), (3, 20, 200)])
+def test_split_path_32_column_walk(B, H, T):
+    # 33 to 127 sequence-heads: the state walk takes 32 value columns per
+    # workgroup (four per sequence-head), one round of workgroups
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, B=B, T=T, H=H, seed=41)
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report(f"split path, 32-column walk B{B} H{H} T{T}", [("o", o, ro), ("S", S, rS)], TOL_BF16)
+
+
 @pytest.mark.parametrize("mode", ["S_final", "no_state", "in_place"])
 def test_piecewise_split_path_batch_ragged(mode):
     # Two sequences (strided windows of the batch), a carried S0 and a ragged

@@ -63,6 +63,7 @@ BASE = W.PREFILL_CONFIGS["batched"]
     ([64, 0, 1, 63, 65, 130, 512, 200, 128, 7, 0, 300, 256, 64, 1, 90], 16, 64),   # fused, 128 cols
     ([700, 1, 0, 129, 512, 33, 64, 260], 24, 128),                               # fused, 64 cols
     ([1000, 0, 2500, 513], 4, 512),                                              # prep + state walk
+    ([900, 1, 0, 300, 129, 64, 65], 12, 64),                    # prep + 32-column state walk
     ([3000], 2, 256),                                                            # one sequence, split
     ([0, 0, 90], 3, 64),                                                         # leading empties
 ])

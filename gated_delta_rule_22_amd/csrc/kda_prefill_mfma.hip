@@ -1197,6 +1197,9 @@ __global__ __launch_bounds__(NCT == 1 ? 832 : 768, 1) void prefill_state_kernel(
     using namespace mf;
     static_assert(NCT == 1 || NCT == 2, "16 or 32 value columns per workgroup");
     constexpr int NT = 8 / NCT;            // workgroups per head
+    // operand sets in flight per wave: one more with two tiles, which fetch
+    // from HBM more often (fewer workgroups share each record through L2)
+    constexpr int PF = NCT == 2 ? mf::PF + 1 : mf::PF;
     constexpr int CW = 16 * NCT;           // value columns per workgroup
     __shared__ bf16x8 sSB[NCT][4][64];     // S as four B operands (32-deep steps), per tile
     __shared__ bf16x4 sUB[NCT][2][64][2];  // U as two B operands, halves by token tile

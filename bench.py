@@ -75,6 +75,82 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def _short_kernel_name(name: str) -> str:
+    """'void kda::prefill_prep_kernel<false, 0, true>(args)' -> 'prefill_prep_kernel<false, 0, true>';
+    a mangled name ('_ZN3kda13decode_kernelI...') -> its unqualified name ('decode_kernel')."""
+    name = name.strip().replace("(anonymous namespace)::", "")
+    if name.startswith("_ZN"):
+        parts, i = [], 3
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            parts.append(name[j:j + n])
+            i = j + n
+        return parts[-1] if parts else name
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    name = name[:cut]
+    return name.split("::")[-1] if "<" not in name else name.replace("kda::", "")
+
+
+def record_traffic(workload: str, fetch_dir: str, write_dir: str, calls: int) -> dict:
+    """Write the HBM bytes per call of one workload into profiles/traffic.json
+    from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; csv output)
+    over `calls` calls of that workload, for the kernels of the kda library
+    (the decode kernel alone for `decode`). Each counter is averaged per
+    dispatch, scaled by the factor recorded from a plain device copy, and
+    summed over the dispatches of one call."""
+    import csv
+    import glob
+    import workloads as W
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        tot, cnt = {}, {}
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                kn = row["Kernel_Name"]
+                if row["Counter_Name"] != counter or not ("kda::" in kn or kn.startswith("_ZN3kda")):
+                    continue
+                k = _short_kernel_name(row["Kernel_Name"])
+                if workload == "decode" and not k.startswith("decode_kernel"):
+                    continue
+                tot[k] = tot.get(k, 0.0) + float(row["Counter_Value"])
+                cnt[k] = cnt.get(k, 0) + 1
+        return {k: tot[k] / cnt[k] for k in tot}, cnt
+
+    fetch, nf = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, nw = per_kernel(write_dir, "WRITE_SIZE")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path))
+    fs, ws = rec["fetch_scale"], rec["write_scale"]
+    kernels = sorted(fetch)
+    per_call = {k: nf[k] / calls for k in kernels}
+    total = sum((fetch[k] * fs + write.get(k, 0.0) * ws) * 1024 * per_call[k] for k in kernels)
+    cfg = W.DECODE_CONFIGS["decode"] if workload == "decode" else W.PREFILL_CONFIGS[workload]
+    key = ("decode|" if workload == "decode" else "prefill|") + cfg.describe()
+    rec[key] = {"source_hash": kernel_source_hash(), "kernels": kernels,
+                "dispatches_per_call": per_call, "fetch_kib": fetch, "write_kib": write,
+                "bytes_per_launch": total}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec[key]
+
+
 def bench_prefill(cfg, steps, warmup):
     import torch
     import gated_delta_rule_22_amd as kda
@@ -425,7 +501,17 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates "
                          "the HBM byte counters against a known traffic)")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: store the HBM bytes per call of WORKLOAD (prefill, "
+                         "batched, long or decode) in profiles/traffic.json from the csv "
+                         "output of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--calls", type=int, default=3,
+                    help="calls of the workload in those runs (with --record-traffic)")
     args = ap.parse_args()
+    if args.record_traffic:
+        wl, fd, wd = args.record_traffic
+        print(json.dumps(record_traffic(wl, fd, wd, args.calls)))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the KDA path here "

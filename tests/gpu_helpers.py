@@ -40,11 +40,11 @@ def per_head_rel_l2(got, ref, axes):
     """Largest rel-L2 over the (sequence, head) slices (the recurrences are
     independent per head, so a head is the natural unit of error)."""
     x, r = _f64(got), _f64(ref)
+    if x.size == 0:          # no tokens (or no heads): nothing to compare
+        return 0.0, 0
     rest = [a for a in range(x.ndim) if a not in axes]
     x = np.transpose(x, list(axes) + rest).reshape(-1, int(np.prod([x.shape[a] for a in rest])))
     r = np.transpose(r, list(axes) + rest).reshape(x.shape)
-    if x.shape[1] == 0:
-        return 0.0, 0
     nr = np.linalg.norm(r, axis=1)
     nd = np.linalg.norm(x - r, axis=1)
     amax = np.max(np.abs(x - r), axis=1)

@@ -33,6 +33,8 @@ constexpr int TM = 8;             // most draft tokens
 constexpr float kLogDecayFloor = -10.f;   // TM * 10 = 80 < 88 (fp32 exp range)
 constexpr int AS = D + 8;         // bf16 row stride of [16][D] operand tiles
 constexpr int RS = 16 + 8;        // bf16 row stride of K_restore^T [D][16 token slots]
+constexpr int RT = 32 + 4;        // fp32 row stride of a wave's [16][32] commit staging block
+constexpr int kStageFloats = 4 * 16 * RT;   // four waves
 
 // Buffer resource word 3 for raw 32-bit accesses on CDNA, and the cache
 // policy bit of a streaming (non-temporal) access. The b32 buffer builtins
@@ -78,16 +80,11 @@ __device__ __forceinline__ void row_swap(f32x4& a, f32x4& b) {
 }
 
 // Two 8-row loads (lane rows: 16-column tile 0 and 1 of rows +0..3, then the
-// same of rows +4..7) -> the two accumulator tiles of those 16 rows; and back.
+// same of rows +4..7) -> the two accumulator tiles of those 16 rows.
 __device__ __forceinline__ void tiles_from_rows(f32x4& a, f32x4& b) {
     a = quad_transpose(a);
     b = quad_transpose(b);
     row_swap(a, b);
-}
-__device__ __forceinline__ void rows_from_tiles(f32x4& a, f32x4& b) {
-    row_swap(a, b);
-    a = quad_transpose(a);
-    b = quad_transpose(b);
 }
 
 __device__ __forceinline__ bf16x8 ldA_perm8(const bf16* rowp, int k0, int g) {
@@ -112,7 +109,9 @@ __global__ __launch_bounds__(256, 4) void decode_multi_mfma_kernel(
     KDA_LDS float sKd[TM * D];
     KDA_LDS float sQd[TM * D];
     KDA_LDS float sKi[TM * D];
-    KDA_LDS float sW[16 * D];      // [K_decay; Q_decay] S
+    // [K_decay; Q_decay] S; once U and O are formed, the committing pass's
+    // per-wave [16][RT] row-major staging of the updated tiles
+    KDA_LDS float sW[kStageFloats > 16 * D ? kStageFloats : 16 * D];
     KDA_LDS float sL[TM * TM];
     KDA_LDS float sM[TM * TM];
     KDA_LDS float sDal[D];
@@ -135,8 +134,9 @@ __global__ __launch_bounds__(256, 4) void decode_multi_mfma_kernel(
     // that st[m][ct] is an MFMA accumulator tile: lane (g, r) holds column
     // c0 + 16ct + r of rows 16m + 4 sig(g) + i, sig(g) = (0, 2, 1, 3)[g]
     // (the A operands below index their rows with the same permutation). The
-    // store runs the steps backwards. Buffer accesses: a per-head resource,
-    // one per-lane byte offset and a uniform offset per 8-row load.
+    // committed tiles return to the row pieces through LDS for the store.
+    // Buffer accesses: a per-head resource, one per-lane byte offset and a
+    // uniform offset per 8-row load.
     float* Sh = S + (size_t)head * D * D;
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(Sh, 0, D * D * 4, kBufWord3);
     const int c0 = 32 * wave;
@@ -292,6 +292,13 @@ __global__ __launch_bounds__(256, 4) void decode_multi_mfma_kernel(
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) b[ct][i] = __builtin_bit_cast(short, sU[(4 * g + i) * AS + c0 + 16 * ct + r]);
+    // The updated tiles go back to the row pieces of the loads through a
+    // per-wave LDS block (sW is dead after the barrier above) rather than by
+    // lane permutes: v_permlane16_swap on matrix-core results, followed by
+    // the quad transposes, left stale values in the last lane of a 16-lane
+    // row now and then on gfx950 (about 7 of 8192 heads per call).
+    float* tb = sW + wave * (16 * RT);
+    const int prow = 4 * (lane >> 5) + (lane & 3), pcol = 4 * ((lane >> 2) & 7);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         // (accumulator row 4g + i is state row 16m + 4 sig(g) + i; the A
@@ -299,13 +306,19 @@ __global__ __launch_bounds__(256, 4) void decode_multi_mfma_kernel(
         const f32x4 dal = *reinterpret_cast<const f32x4*>(&sDal[16 * m + 4 * sig]);
         const int ar = 4 * (((r >> 2) & 1) << 1 | (r >> 3)) + (r & 3);
         const s16x4 a = *reinterpret_cast<const s16x4*>(&sKrT[(16 * m + ar) * RS + 4 * g]);
-        f32x4 t0 = mma16(a, b[0], st[m][0] * dal);
-        f32x4 t1 = mma16(a, b[1], st[m][1] * dal);
-        rows_from_tiles(t0, t1);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t0), srs, off,
-                                               (2 * m) * 8 * D * 4, kNT);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t1), srs, off,
-                                               (2 * m + 1) * 8 * D * 4, kNT);
+        const f32x4 t[2] = {mma16(a, b[0], st[m][0] * dal), mma16(a, b[1], st[m][1] * dal)};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tb[(4 * sig + i) * RT + 16 * ct + r] = t[ct][i];
+        lds_fence_wave();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 y = *reinterpret_cast<const f32x4*>(&tb[(8 * h + prow) * RT + pcol]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), srs, off,
+                                                   (2 * m + h) * 8 * D * 4, kNT);
+        }
+        lds_fence_wave();   // the block's reads are done before the next tile's writes
     }
 }
 

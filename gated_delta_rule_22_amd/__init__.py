@@ -216,7 +216,9 @@ def kda_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     cu_seqlens int32 [N+1] on the device; S0 [N,H,dk,dv] fp32 or None. With
     ckpt_every > 0 (a multiple of 64) the state after every ckpt_every tokens
     of each sequence goes to S_ckpt [ckpt_slots,H,dk,dv] (default
-    T // ckpt_every slots). Returns (o [T,H,dv], S_final or None, S_ckpt or None)."""
+    T // ckpt_every slots, allocated uninitialised: only the first
+    sum(len_i // ckpt_every) of them are written). Returns (o [T,H,dv],
+    S_final or None, S_ckpt or None)."""
     lib = load_library()
     T, H, dk = q.shape
     dv = v.shape[-1]

@@ -135,7 +135,9 @@ size_t kda_prefill_varlen_workspace_size(int N, int T_total, int H, int dk, int 
  *            S_ckpt [ckpt_slots,H,dk,dv] fp32. Sequence i's checkpoints j = 1
  *            .. len_i / ckpt_every take slots c_i + j - 1, where c_i is the
  *            sum of len / ckpt_every over the sequences before i. Slots
- *            at or past ckpt_slots are not written. T_total / ckpt_every
+ *            at or past ckpt_slots are not written, nor are the slots past
+ *            the last checkpoint (sum over all sequences of len /
+ *            ckpt_every), which keep their contents. T_total / ckpt_every
  *            slots always suffice. With ckpt_every = 0, S_ckpt and
  *            ckpt_slots are ignored.
  *   ws, ws_bytes  device workspace, 256-byte aligned, at least

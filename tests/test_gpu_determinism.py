@@ -93,10 +93,13 @@ def test_layer_forms_repeatable():
     _same("layer prefill 4K, bounded gate + L2 + norm-gate", lambda: kda.kda_prefill_layer(
         lx["q"], lx["k"], lx["v"], lx["g"], lx["beta"], None, gate_mode=kda.KDA_GATE_BOUNDED,
         l2norm=True, z=lx["z"], w=lx["w"]))
-    lb = W.layer_inputs(W.PREFILL_CONFIGS["batched"], B=2, T=500, device=DEV)
-    _same("layer prefill B2 H32 T500 (fused epilogue)", lambda: kda.kda_prefill_layer(
-        lb["q"], lb["k"], lb["v"], lb["g"], lb["beta"], None, gate_mode=kda.KDA_GATE_BOUNDED,
-        l2norm=True, z=lb["z"], w=lb["w"]))
+    # 64 sequence-heads: split path and the separate epilogue kernel;
+    # 256: the 128-column fused kernel with the epilogue in registers
+    for B in (2, 8):
+        lb = W.layer_inputs(W.PREFILL_CONFIGS["batched"], B=B, T=300, device=DEV)
+        _same(f"layer prefill B{B} H32 T300", lambda: kda.kda_prefill_layer(
+            lb["q"], lb["k"], lb["v"], lb["g"], lb["beta"], None, gate_mode=kda.KDA_GATE_BOUNDED,
+            l2norm=True, z=lb["z"], w=lb["w"]))
     dc = W.DECODE_CONFIGS["decode"]
     S0 = W.decode_state(dc, device=DEV)
     ld = W.layer_inputs(dataclasses.replace(W.PREFILL_CONFIGS["prefill"]), B=dc.B, H=dc.H,

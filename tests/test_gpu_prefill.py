@@ -443,3 +443,23 @@ def test_prefill_then_decode_equals_prefill_of_concatenation(H):
             ("S", S, S_all.cpu().double().numpy())], TOL_BF16)
     ro, rS = oracle_prefill(x)
     report(f"prefill + decode vs oracle, H{H}", [("o", o_dec, ro[:, T:]), ("S", S, rS)], TOL_BF16)
+
+
+@pytest.mark.parametrize("H", [65536, 65537])
+def test_head_count_limit(H):
+    """The matrix-core prefill takes up to 65536 heads per token row: its
+    chunk loads address one chunk of every head through 32-bit buffer
+    offsets, and at 65536 heads the 64 log-decay rows of a chunk span just
+    under 2^31 bytes. One head more takes the generic bf16 kernel. Both at
+    one full chunk plus a one-token chunk (the largest offsets of the first
+    chunk, then a ragged tail), checked on sampled heads, the last included."""
+    c = W.PREFILL_CONFIGS["prefill"]
+    xd = W.prefill_inputs(c, B=1, T=65, H=H, seed=65, device=DEV)
+    o, S = gpu_prefill(xd, S0=None)
+    heads = [0, 1, H // 2, H - 2, H - 1]
+    x = {n: (t[:, :, heads].cpu() if t is not None else None) for n, t in xd.items()}
+    ro, rS = oracle_prefill(x, S0=None)
+    report(f"head-count limit B1 T65 H{H}, heads {heads}",
+           [("o", o[:, :, heads], ro), ("S", S[:, heads], rS)], TOL_BF16)
+    del xd, o, S
+    torch.cuda.empty_cache()

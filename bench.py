@@ -625,7 +625,8 @@ def main():
 
     if not args.no_cpu:
         _log("[bench] cpu oracle baseline")
-        # the machine's CPU share (OMP_NUM_THREADS there), not the host's count
+        # the CPU share this process may use (OMP_NUM_THREADS when set), which
+        # can be smaller than the machine's core count
         cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
                     or (os.cpu_count() or 1))
         result["cpu_baseline"] = cpu_baseline_prefill(cfg, max_heads=cores)

@@ -52,6 +52,19 @@ def test_fp32_shapes_ragged(dk, dv, T, chunk):
     report(f"fp32 dk{dk} dv{dv} T{T} C{chunk}", [("o", o, ro), ("S", S, rS)], TOL_F32)
 
 
+@pytest.mark.parametrize("base,B,H,T", [("prefill", 1, 16, 4096), ("batched", 2, 8, 2000)])
+def test_fp32_at_config_size(base, B, H, T):
+    """fp32 inputs at the 4K configuration's full size (and a ragged batch
+    with the batched configuration's carried state and decay mix): 64 chunks
+    of fp32 state carry on the generic kernel, every head, against the
+    fp32 bar."""
+    c = W.PREFILL_CONFIGS[base]
+    x = W.prefill_inputs(c, B=B, T=T, H=H, dtype=torch.float32)
+    o, S = gpu_prefill(to_dev(x))
+    ro, rS = oracle_prefill(x)
+    report(f"fp32 {base} B{B} H{H} T{T}", [("o", o, ro), ("S", S, rS)], TOL_F32)
+
+
 @pytest.mark.parametrize("T", [1, 17, 64, 200, 256])
 def test_bf16_mfma_small(T):
     c = W.PREFILL_CONFIGS["batched"]

@@ -426,11 +426,23 @@ def bench_layer(cfg, reps=20):
     return out
 
 
+def traffic_rate(traffic, kernel_us):
+    """The measured HBM bytes per launch over the same launch time: how close
+    the kernels run to the memory system for the bytes they actually move
+    (None when the counters do not match the current sources)."""
+    if traffic is None:
+        return {"traffic_gbps": None, "traffic_frac": None}
+    gbs = traffic / (kernel_us * 1e-6) / 1e9
+    return {"traffic_gbps": gbs, "traffic_frac": gbs / HBM_PEAK_GBS}
+
+
 def prefill_roofline(pre, workload):
     kernels = ("prefill_prep_kernel + prefill_state_kernel" if pre["workspace_bytes"] > 0
                else "prefill_fused_kernel")
+    traffic = measured_traffic("prefill", workload)
     return {"bound": "hbm", "achieved": pre["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": pre["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic("prefill", workload),
+            "frac": pre["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+            **traffic_rate(traffic, pre["kernel_ms"] * 1e3),
             "kernel": kernels, "kernel_us": pre["kernel_ms"] * 1e3,
             "algorithmic_bytes": pre["bytes"]}
 
@@ -589,12 +601,13 @@ def main():
         _log(f"[bench] decode {dc.describe()}")
         dec = bench_decode(dc)
         _log(f"[bench] decode {dec['kernel_us']:.1f} us/step, {dec['gbs']:.0f} GB/s")
+        dtraffic = measured_traffic("decode", dc.describe())
         result["decode"] = {
             "workload": dc.describe(), "steps_per_s": dec["steps_per_s"],
             "tokens_per_s": dec["tokens_per_s"], "us_per_step": dec["wall_s"] / dec["steps"] * 1e6,
             "roofline": {"bound": "hbm", "achieved": dec["gbs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": dec["gbs"] / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("decode", dc.describe()),
+                         "traffic": dtraffic, **traffic_rate(dtraffic, dec["kernel_us"]),
                          "kernel": "decode_kernel", "kernel_us": dec["kernel_us"],
                          "algorithmic_bytes": dec["bytes_per_step"]},
         }

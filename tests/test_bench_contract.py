@@ -81,3 +81,12 @@ def test_record_traffic_from_counter_csv(tmp_path, monkeypatch):
     saved = json.load(open(tmp_path / "profiles" / "traffic.json"))
     key = next(k for k in saved if k.startswith("prefill|") and "T1048576" in k)
     assert saved[key] == rec
+
+
+def test_traffic_rate():
+    bench = _bench_module()
+    # 128 GB moved in 25.6 ms is 5 TB/s, 62.5% of the 8 TB/s peak
+    r = bench.traffic_rate(128e9, 25.6e3)
+    assert abs(r["traffic_gbps"] - 5000.0) < 1e-6
+    assert abs(r["traffic_frac"] - 0.625) < 1e-9
+    assert bench.traffic_rate(None, 25.6e3) == {"traffic_gbps": None, "traffic_frac": None}

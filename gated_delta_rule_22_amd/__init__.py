@@ -113,6 +113,18 @@ def _stream(stream, device) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream) -> torch.Tensor:
+    """A tensor this binding allocates for a call (an output the caller left
+    out, or the workspace). torch's caching allocator ties it to the current
+    stream; a call on another stream records that stream on it too, so that
+    its memory is not handed out again, once the caller or this binding drops
+    the tensor, before the call's kernels on that stream have finished."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
 def kda_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int,
                                dtype: torch.dtype, chunk: int = 64) -> int:
     return int(load_library().kda_prefill_workspace_size(B, T, H, dk, dv, _DTYPES[dtype], chunk))
@@ -143,15 +155,15 @@ def kda_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if S0 is not None:
         _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+        o = _empty((B, T, H, dv), dt, dev, stream)
     _check(o, "o", (B, T, H, dv), dt, dev)
     if S_final is None and want_state:
-        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        S_final = _empty((B, H, dk, dv), torch.float32, dev, stream)
     if S_final is not None:
         _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     ws_bytes = kda_prefill_workspace_size(B, T, H, dk, dv, dt, chunk)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _empty(ws_bytes, torch.uint8, dev, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
                              _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
@@ -240,23 +252,23 @@ def kda_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if S0 is not None:
         _check(S0, "S0", (N, H, dk, dv), torch.float32, dev)
     if o is None:
-        o = torch.empty((T, H, dv), dtype=dt, device=dev)
+        o = _empty((T, H, dv), dt, dev, stream)
     _check(o, "o", (T, H, dv), dt, dev)
     if S_final is None and want_state:
-        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        S_final = _empty((N, H, dk, dv), torch.float32, dev, stream)
     if S_final is not None:
         _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
     if ckpt_every > 0:
         if ckpt_slots is None:
             ckpt_slots = S_ckpt.shape[0] if S_ckpt is not None else max(T // ckpt_every, 1)
         if S_ckpt is None:
-            S_ckpt = torch.empty((ckpt_slots, H, dk, dv), dtype=torch.float32, device=dev)
+            S_ckpt = _empty((ckpt_slots, H, dk, dv), torch.float32, dev, stream)
         _check(S_ckpt, "S_ckpt", (ckpt_slots, H, dk, dv), torch.float32, dev)
     else:
         ckpt_slots, S_ckpt = 0, None
     ws_bytes = kda_prefill_varlen_workspace_size(N, T, H, dk, dv, dt, chunk)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _empty(ws_bytes, torch.uint8, dev, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                 _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), N, T, H,
@@ -287,7 +299,7 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check(beta, "beta", (B, H), torch.float32, dev)
     _check(S, "S", (B, H, dk, dv), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+        o = _empty((B, H, dv), dt, dev, stream)
     _check(o, "o", (B, H, dv), dt, dev)
     st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
                              _ptr(o), B, H, dk, dv, _DTYPES[dt], _stream(stream, dev))
@@ -322,7 +334,7 @@ def kda_decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if n_commit is not None:
         _check(n_commit, "n_commit", (B,), torch.int32, dev)
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+        o = _empty((B, T, H, dv), dt, dev, stream)
     _check(o, "o", (B, T, H, dv), dt, dev)
     st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
                               _ptr(o), _ptr(n_commit), B, T, H, dk, dv, _DTYPES[dt],
@@ -383,15 +395,15 @@ def kda_prefill_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: t
     if S0 is not None:
         _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+        o = _empty((B, T, H, dv), dt, dev, stream)
     _check(o, "o", (B, T, H, dv), dt, dev)
     if S_final is None and want_state:
-        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        S_final = _empty((B, H, dk, dv), torch.float32, dev, stream)
     if S_final is not None:
         _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     ws_bytes = kda_prefill_workspace_size(B, T, H, dk, dv, dt, chunk)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _empty(ws_bytes, torch.uint8, dev, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     opts = _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps)
     st = lib.kda_prefill_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
@@ -426,7 +438,7 @@ def kda_decode_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: to
     _check(S, "S", (B, H, dk, dv), torch.float32, dev)
     _check_layer_extra(gate, gate_mode, (B, H), dk, dv, dt, dev, z, w)
     if o is None:
-        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+        o = _empty((B, H, dv), dt, dev, stream)
     _check(o, "o", (B, H, dv), dt, dev)
     opts = _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps)
     st = lib.kda_decode_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),

@@ -165,9 +165,10 @@ def kda_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = _empty(ws_bytes, torch.uint8, dev, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.kda_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                             _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
-                             _ptr(workspace), wsz, _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                                 _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
+                                 _ptr(workspace), wsz, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_fwd")
     return o, S_final
@@ -203,9 +204,10 @@ def kda_prefill_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check(o, "o", (B, T, H, dv), dt, dev)
     if S_final is not None:
         _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
-    st = lib.kda_prefill_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                     _ptr(S0), _ptr(o), _ptr(S_final), B, T, H, dk, dv,
-                                     _DTYPES[dt], chunk, _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_prefill_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                         _ptr(S0), _ptr(o), _ptr(S_final), B, T, H, dk, dv,
+                                         _DTYPES[dt], chunk, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_fwd_noalloc")
 
@@ -270,10 +272,11 @@ def kda_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = _empty(ws_bytes, torch.uint8, dev, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), N, T, H,
-                                dk, dv, _DTYPES[dt], chunk, _ptr(S_ckpt), int(ckpt_every),
-                                int(ckpt_slots), _ptr(workspace), wsz, _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                    _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), N, T, H,
+                                    dk, dv, _DTYPES[dt], chunk, _ptr(S_ckpt), int(ckpt_every),
+                                    int(ckpt_slots), _ptr(workspace), wsz, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_varlen")
     return o, S_final, S_ckpt
@@ -301,8 +304,9 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if o is None:
         o = _empty((B, H, dv), dt, dev, stream)
     _check(o, "o", (B, H, dv), dt, dev)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
-                             _ptr(o), B, H, dk, dv, _DTYPES[dt], _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                 _ptr(o), B, H, dk, dv, _DTYPES[dt], _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_decode_step")
     return o
@@ -336,9 +340,10 @@ def kda_decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if o is None:
         o = _empty((B, T, H, dv), dt, dev, stream)
     _check(o, "o", (B, T, H, dv), dt, dev)
-    st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
-                              _ptr(o), _ptr(n_commit), B, T, H, dk, dv, _DTYPES[dt],
-                              _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                  _ptr(o), _ptr(n_commit), B, T, H, dk, dv, _DTYPES[dt],
+                                  _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_decode_multi")
     return o
@@ -406,9 +411,10 @@ def kda_prefill_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: t
         workspace = _empty(ws_bytes, torch.uint8, dev, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     opts = _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps)
-    st = lib.kda_prefill_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
-                               _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
-                               ctypes.byref(opts), _ptr(workspace), wsz, _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_prefill_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S0),
+                                   _ptr(o), _ptr(S_final), B, T, H, dk, dv, _DTYPES[dt], chunk,
+                                   ctypes.byref(opts), _ptr(workspace), wsz, _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_prefill_layer")
     return o, S_final
@@ -441,9 +447,10 @@ def kda_decode_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: to
         o = _empty((B, H, dv), dt, dev, stream)
     _check(o, "o", (B, H, dv), dt, dev)
     opts = _layer_opts(gate_mode, decay_bound, l2norm, l2_eps, z, w, out_eps)
-    st = lib.kda_decode_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
-                              _ptr(o), B, H, dk, dv, _DTYPES[dt], ctypes.byref(opts),
-                              _stream(stream, dev))
+    with torch.cuda.device(dev):
+        st = lib.kda_decode_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
+                                  _ptr(o), B, H, dk, dv, _DTYPES[dt], ctypes.byref(opts),
+                                  _stream(stream, dev))
     if st != 0:
         raise KDAError(st, "kda_decode_layer")
     return o

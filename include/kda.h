@@ -23,8 +23,11 @@
  * memory in these calls, never frees and never synchronises; work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
  * asynchronously, so a device fault surfaces at the caller's next
- * synchronisation. The library keeps no state between calls and is
- * reentrant.
+ * synchronisation. Every pointer must be memory of the calling thread's
+ * current HIP device, and `stream` a stream of that device: kernels launch
+ * there (and kda_prefill_fwd_noalloc uses that device's scratch array). The
+ * library keeps no state between calls apart from that array and its
+ * cached address, and is reentrant.
  *
  * Errors: every argument is validated on the host before anything is
  * launched; a rejected call has no side effect. KDA_ERR_HIP reports a launch

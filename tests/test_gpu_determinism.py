@@ -41,6 +41,24 @@ def test_prefill_repeatable(B, T, H):
           lambda: kda.kda_prefill_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"]))
 
 
+def test_batched_config_repeatable():
+    # B8 H32 T8192 with carried state: the fused kernel at full size
+    c = W.PREFILL_CONFIGS["batched"]
+    x = W.prefill_inputs(c, device=DEV)
+    _same("batched configuration B8 H32 T8192",
+          lambda: kda.kda_prefill_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"]))
+
+
+def test_long_config_repeatable():
+    # B1 H32 T1048576: 171 pieces of prep and state walk, every output element
+    c = W.PREFILL_CONFIGS["long"]
+    x = W.prefill_inputs_by_head(c, device=DEV)
+    _same("1M-token configuration B1 H32",
+          lambda: kda.kda_prefill_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None))
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_piecewise_prefill_repeatable():
     c = W.PREFILL_CONFIGS["long"]
     x = W.prefill_inputs_by_head(c, T=1 << 17, device=DEV)

@@ -92,6 +92,8 @@ def split_slots(ws, N):
     ([64, 2048, 64, 64, 1, 64, 64, 64], 32, 0, [1]),              # m = 5 chunks
     ([64, 2048, 64, 64, 1, 64, 64, 64], 32, 512, [1]),            # m = 8: one checkpoint each side
     ([3000, 100, 0, 65, 2500] + [64] * 11, 16, 128, [0, 4]),      # two split, ragged ends
+    ([3000, 64, 500, 64], 128, 256, [0]),                          # room for one split sequence
+    ([5000, 64, 4000, 64, 3000, 64], 64, 512, [0, 2]),            # 47 chunks: under the share of 48
 ])
 def test_bf16_split_schedule(lengths, H, ckpt, split):
     x = W.varlen_inputs(BASE, lengths, H=H, seed=31)

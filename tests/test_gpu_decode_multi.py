@@ -59,6 +59,19 @@ def test_multi_fp32_shapes(dk, dv):
     report(f"multi fp32 dk{dk} dv{dv} T5 n={n}", [("o", o, ro), ("S", S, rS)], TOL_F32)
 
 
+@pytest.mark.parametrize("dtype,T", [(torch.bfloat16, 12), (torch.bfloat16, 33), (torch.float32, 20)])
+def test_long_drafts_on_the_valu_kernel(dtype, T):
+    # drafts past 8 tokens (and fp32 ones) take the VALU kernel
+    B, H = 6, 8
+    x = inputs(B, T, H, dtype=dtype, seed=40 + T)
+    n = [int(v) for v in torch.randint(0, T + 1, (B,), generator=torch.Generator().manual_seed(T))]
+    n[0], n[1] = 0, T
+    o, S = gpu_multi(x, n)
+    ro, rS = oracle_multi(x, n)
+    report(f"multi {dtype} B{B} H{H} T{T} n={n}", [("o", o, ro), ("S", S, rS)],
+           TOL_F32 if dtype == torch.float32 else TOL_BF16)
+
+
 def test_multi_bf16_random_accept():
     B, T, H = 8, 8, 32
     x = inputs(B, T, H, seed=21)
